@@ -1,0 +1,128 @@
+"""ctypes wrapper around the plain-C fp64 oracle (``ssm_oracle.c``).
+
+Test infrastructure only (see the package docstring). Arrays are numpy
+float64, C-contiguous, in the layouts documented in ``ssm_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SRC = os.path.join(HERE, "ssm_oracle.c")
+ORACLE_LIB = os.path.join(HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build_oracle(src: str = ORACLE_SRC, out: str = ORACLE_LIB) -> str:
+    """Compile the oracle with gcc (fp64, -O2, OpenMP, no fast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_dp)
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        a = a.reshape(shape)
+    return a
+
+
+class Oracle:
+    """Thin handle on one compiled oracle library (the real one or a test
+    mutant built from an edited copy of the source)."""
+
+    def __init__(self, lib_path: str = ORACLE_LIB):
+        self.path = lib_path
+        lib = ctypes.CDLL(lib_path)
+        lib.oracle_scan_f64.restype = ctypes.c_int
+        lib.oracle_scan_f64.argtypes = [_i64, _i64, _i64, _i64] + [_dp] * 9 + \
+            [ctypes.c_int, _dp, _dp, ctypes.c_int]
+        lib.oracle_state_update_f64.restype = ctypes.c_int
+        lib.oracle_state_update_f64.argtypes = [_i64, _i64, _i64] + [_dp] * 9 + \
+            [ctypes.c_int, _dp, ctypes.c_int]
+        self.lib = lib
+
+    def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+             zoh=False, nthreads=None):
+        """Full-sequence scan. x, delta, z: (batch, L, dim); A: (dim, N);
+        B, C: (batch, L, N); D, delta_bias: (dim,); h0: (batch, dim, N).
+        Returns (out (batch, L, dim), last_state (batch, dim, N)) in fp64."""
+        x = _f64(x)
+        batch, L, dim = x.shape
+        A = _f64(A)
+        N = A.shape[1]
+        delta = _f64(delta, x.shape)
+        B = _f64(B, (batch, L, N))
+        C = _f64(C, (batch, L, N))
+        D = _f64(D, (dim,))
+        z = _f64(z, x.shape)
+        delta_bias = _f64(delta_bias, (dim,))
+        h0 = _f64(h0, (batch, dim, N))
+        out = np.empty((batch, L, dim), dtype=np.float64)
+        last = np.empty((batch, dim, N), dtype=np.float64)
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_scan_f64(batch, L, dim, N, _ptr(x), _ptr(delta), _ptr(A),
+                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                      _ptr(h0), int(bool(zoh)), _ptr(out), _ptr(last), nt)
+        if rc != 0:
+            raise ValueError("oracle_scan_f64 returned %d" % rc)
+        return out, last
+
+    def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     zoh=False, nthreads=None):
+        """One decode token. state: (batch, dim, N), updated copy returned;
+        x, delta, z: (batch, dim); B, C: (batch, N). Returns (out, new_state)."""
+        x = _f64(x)
+        batch, dim = x.shape
+        A = _f64(A)
+        N = A.shape[1]
+        st = np.array(_f64(state, (batch, dim, N)), dtype=np.float64, copy=True)
+        delta = _f64(delta, x.shape)
+        B = _f64(B, (batch, N))
+        C = _f64(C, (batch, N))
+        D = _f64(D, (dim,))
+        z = _f64(z, x.shape)
+        delta_bias = _f64(delta_bias, (dim,))
+        out = np.empty((batch, dim), dtype=np.float64)
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_state_update_f64(batch, dim, N, _ptr(st), _ptr(x), _ptr(delta),
+                                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                              _ptr(delta_bias), int(bool(zoh)), _ptr(out), nt)
+        if rc != 0:
+            raise ValueError("oracle_state_update_f64 returned %d" % rc)
+        return out, st
+
+
+_default = None
+_lock = threading.Lock()
+
+
+def default_oracle() -> Oracle:
+    """The oracle built from ``ssm_oracle.c``; compiled on first use if the
+    library is missing or older than its source."""
+    global _default
+    with _lock:
+        if _default is None:
+            if (not os.path.exists(ORACLE_LIB)
+                    or os.path.getmtime(ORACLE_LIB) < os.path.getmtime(ORACLE_SRC)):
+                build_oracle()
+            _default = Oracle(ORACLE_LIB)
+        return _default

@@ -1,0 +1,155 @@
+/*
+ * fp64 CPU oracle for the selective state-space scan (S6) and its one-token
+ * state update.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this file: only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg use it. It shares no code, header or constant with the HIP
+ * library; it is a plain, slow, literal restatement of what the pages define.
+ *
+ * What it computes, for every batch row b and channel d independently (one SSM
+ * per channel: erikxu.me "Mamba" notes, section "State Space Models", the
+ * paragraph on multidimensional inputs; ai.thesatyajit.com "Mamba and
+ * selective state spaces", section "A state space model": the state of a
+ * layer is D x N numbers):
+ *
+ *   h_{-1} = 0 (or a given initial state)          erikxu.me, "State Space
+ *                                                   Models", discrete system
+ *   for t = 0 .. L-1:
+ *     Delta_t = softplus(delta[b,t,d] + bias[d])    ai.thesatyajit.com,
+ *                                                   "Selection: B, C and Delta
+ *                                                   from the token"
+ *     abar_n  = exp(Delta_t * A[d,n])               same page, "Discretisation:
+ *                                                   zero-order hold" and
+ *                                                   "Selection" (A acts only
+ *                                                   through exp(Delta A))
+ *     bbar_n  = Delta_t * B[b,t,n]                  "Discretisation": the
+ *                                                   first-order B-bar that the
+ *                                                   reference code computes
+ *             (or (abar_n - 1) / A[d,n] * B[b,t,n]  exact zero-order hold, a
+ *                                                   test-only mode)
+ *     h_n     = abar_n * h_n + bbar_n * x[b,t,d]    recurrence h_t = A-bar
+ *                                                   h_{t-1} + B-bar x_t
+ *     y       = sum_n C[b,t,n] * h_n + D[d] * x     y_t = C h_t + D x_t
+ *                                                   (datarekha.com "State space
+ *                                                   models and Mamba", "One
+ *                                                   system, two views")
+ *     y      *= silu(z[b,t,d]) if z is given        ai.thesatyajit.com, "The
+ *                                                   Mamba block": the SSM
+ *                                                   branch is multiplied by a
+ *                                                   SiLU gate
+ *   last_state[b,d,:] = h
+ *
+ * Layouts (row-major, contiguous): x, delta, z, out: (batch, seqlen, dim);
+ * B, C: (batch, seqlen, dstate), one group shared by every channel; A:
+ * (dim, dstate); D, bias: (dim); h0, last_state, state: (batch, dim, dstate).
+ * Optional arguments are NULL when absent (no D skip, no gate, zero bias, zero
+ * initial state, no final state).
+ *
+ * Every value is double precision; libm exp/log1p; no fast-math.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* softplus(u) = log(1 + exp(u)), written so that neither branch overflows. */
+static double softplus(double u) {
+  if (u > 0.0) return u + log1p(exp(-u));
+  return log1p(exp(u));
+}
+
+/* silu(v) = v * sigmoid(v) = v / (1 + exp(-v)). */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* One token of one (b, d) row: updates h[0..N-1] in place, returns y. */
+static double row_step(int64_t N, double *h, double x, double delta_raw,
+                       double bias, const double *A_d, const double *B_t,
+                       const double *C_t, const double *D_d, const double *z,
+                       int zoh) {
+  double Delta = softplus(delta_raw + bias);
+  double y = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    double abar = exp(Delta * A_d[n]);
+    double bbar;
+    if (zoh)
+      bbar = (abar - 1.0) / A_d[n] * B_t[n];
+    else
+      bbar = Delta * B_t[n];
+    h[n] = abar * h[n] + bbar * x;
+    y += C_t[n] * h[n];
+  }
+  if (D_d) y += (*D_d) * x;
+  if (z) y *= silu(*z);
+  return y;
+}
+
+/*
+ * Full-sequence scan. Returns 0 on success, -1 on bad sizes or a missing
+ * required pointer, -2 when zoh is requested with a zero entry of A.
+ */
+int oracle_scan_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    const double *x, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D,
+                    const double *z, const double *delta_bias,
+                    const double *h0, int zoh, double *out, double *last_state,
+                    int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return -1;
+  if (!x || !delta || !A || !B || !C || !out) return -1;
+  if (zoh)
+    for (int64_t i = 0; i < dim * dstate; ++i)
+      if (A[i] == 0.0) return -2;
+  if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double *h = (double *)malloc(sizeof(double) * (size_t)dstate);
+      for (int64_t n = 0; n < dstate; ++n)
+        h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+      double bias = delta_bias ? delta_bias[d] : 0.0;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        int64_t i = (b * seqlen + t) * dim + d;   /* (b, t, d) */
+        int64_t j = (b * seqlen + t) * dstate;    /* (b, t, 0) */
+        out[i] = row_step(dstate, h, x[i], delta[i], bias, A + d * dstate,
+                          B + j, C + j, D ? D + d : NULL, z ? z + i : NULL, zoh);
+      }
+      if (last_state)
+        for (int64_t n = 0; n < dstate; ++n)
+          last_state[(b * dim + d) * dstate + n] = h[n];
+      free(h);
+    }
+  }
+  return 0;
+}
+
+/*
+ * One decode token for every (b, d) row: the same step as one iteration of
+ * the scan, against a resident state that is read and written in place.
+ * x, delta, z, out: (batch, dim); B, C: (batch, dstate).
+ */
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate,
+                            double *state, const double *x,
+                            const double *delta, const double *A,
+                            const double *B, const double *C, const double *D,
+                            const double *z, const double *delta_bias, int zoh,
+                            double *out, int nthreads) {
+  if (batch < 0 || dim < 0 || dstate < 1) return -1;
+  if (!state || !x || !delta || !A || !B || !C || !out) return -1;
+  if (zoh)
+    for (int64_t i = 0; i < dim * dstate; ++i)
+      if (A[i] == 0.0) return -2;
+  if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      int64_t i = b * dim + d;
+      out[i] = row_step(dstate, state + i * dstate, x[i], delta[i],
+                        delta_bias ? delta_bias[d] : 0.0, A + d * dstate,
+                        B + b * dstate, C + b * dstate, D ? D + d : NULL,
+                        z ? z + i : NULL, zoh);
+    }
+  }
+  return 0;
+}

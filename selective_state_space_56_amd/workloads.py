@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module is the one piece shared by the HIP path's callers (tests, bench)
+and the oracle's callers: it draws random tensors and holds none of the
+method's arithmetic (no softplus, no exponentials, no recurrence). The shapes
+come from the models the pages discuss: Mamba-2.8B has width 2,560, 5,120 inner
+channels and N = 16 states ("Mamba and selective state spaces, from first
+principles", "The Mamba block"); A starts as the S4D-Real diagonal
+A_n = -(n + 1) (same page, "A state space model").
+
+Distributions, drawn in float32 from one seeded ``torch.Generator`` in the
+order x, Delta_raw, bias, B, C, D, z, then rounded to bfloat16 (round to
+nearest even) where the workload stores bf16:
+  x ~ N(0, 1); Delta_raw ~ N(0, s^2); bias ~ U(log(e^lo - 1), log(e^hi - 1))
+  (uniform in bias space, so softplus(bias) spans [lo, hi]); B, C ~ N(0, 1)
+  shared by all channels of a batch row; D = 1 or U(0.5, 1.5); z ~ N(0, 1).
+Decode workloads add an fp32 initial state h0 ~ N(0, 1) and one token per
+sequence per step.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int          # tokens per scan call (1 for decode)
+    dim: int             # D_inner channels
+    dstate: int          # N
+    io: str              # "f32" or "bf16": storage of x, Delta_raw, z, B, C, y
+    gate: bool           # z present (y * silu(z))
+    d_skip: str          # "one" (D = 1) or "uniform" (D ~ U(0.5, 1.5))
+    delta_lo: float      # softplus(bias) range
+    delta_hi: float
+    delta_std: float     # std of Delta_raw
+    decode_steps: int = 0
+
+    @property
+    def elem_steps(self) -> int:
+        steps = self.decode_steps if self.decode_steps else self.seqlen
+        return self.batch * steps * self.dim
+
+    @property
+    def torch_io(self):
+        return torch.float32 if self.io == "f32" else torch.bfloat16
+
+    def with_shape(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    # tiny fp32 correctness case
+    "tiny_fp32": Workload("tiny_fp32", 1, 256, 64, 16, "f32", False, "one", 0.001, 0.1, 0.5),
+    # Mamba-130M-shaped layer (width 768, expand 2)
+    "mamba130m_layer": Workload("mamba130m_layer", 2, 2048, 1536, 16, "bf16", True, "uniform",
+                                0.001, 0.1, 0.5),
+    # Mamba-2.8B-shaped prefill layer (width 2560, expand 2): the headline workload
+    "mamba2p8b_prefill": Workload("mamba2p8b_prefill", 8, 2048, 5120, 16, "bf16", True, "uniform",
+                                  0.001, 0.1, 0.5),
+    # long context at 2.8B width, small Delta so the state persists
+    "long_context_131k": Workload("long_context_131k", 1, 131072, 5120, 16, "bf16", True, "uniform",
+                                  0.0005, 0.01, 0.5),
+    # batched one-token decode against a resident fp32 state, 64 steps
+    "decode_4096": Workload("decode_4096", 4096, 1, 5120, 16, "bf16", True, "uniform",
+                            0.001, 0.1, 1.0, decode_steps=64),
+}
+
+
+def bias_range(w: Workload):
+    """Endpoints of the uniform bias draw: the bias values whose softplus is
+    delta_lo and delta_hi (inverse of log(1 + e^b), used only to place the
+    draw's endpoints)."""
+    return math.log(math.expm1(w.delta_lo)), math.log(math.expm1(w.delta_hi))
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def make_params(w: Workload, device="cpu", seed=0):
+    """Per-channel parameters A (dim, N), D (dim,), bias (dim,), all fp32.
+    Drawn from their own generator so that decode steps and scans share them."""
+    g = _gen(device, seed + 7919)
+    lo, hi = bias_range(w)
+    bias = torch.rand(w.dim, generator=g, device=device) * (hi - lo) + lo
+    if w.d_skip == "one":
+        D = torch.ones(w.dim, device=device)
+    else:
+        D = torch.rand(w.dim, generator=g, device=device) + 0.5
+    A = -torch.arange(1, w.dstate + 1, dtype=torch.float32, device=device).repeat(w.dim, 1)
+    return {"A": A.contiguous(), "D": D, "delta_bias": bias}
+
+
+def make_scan_inputs(w: Workload, device="cpu", seed=0):
+    """x, delta (Delta_raw), z: (batch, L, dim); B, C: (batch, L, N) in the
+    workload's io dtype; plus make_params(). z is None without a gate."""
+    g = _gen(device, seed)
+    shp = (w.batch, w.seqlen, w.dim)
+    x = torch.randn(shp, generator=g, device=device)
+    delta = torch.randn(shp, generator=g, device=device) * w.delta_std
+    B = torch.randn((w.batch, w.seqlen, w.dstate), generator=g, device=device)
+    C = torch.randn((w.batch, w.seqlen, w.dstate), generator=g, device=device)
+    z = torch.randn(shp, generator=g, device=device) if w.gate else None
+    io = w.torch_io
+    out = {"x": x.to(io), "delta": delta.to(io), "B": B.to(io), "C": C.to(io),
+           "z": None if z is None else z.to(io)}
+    out.update(make_params(w, device, seed))
+    return out
+
+
+def make_decode_state(w: Workload, device="cpu", seed=0):
+    """Initial fp32 state h0 ~ N(0, 1), (batch, dim, N)."""
+    g = _gen(device, seed + 104729)
+    return torch.randn((w.batch, w.dim, w.dstate), generator=g, device=device)
+
+
+def make_decode_token(w: Workload, step: int, device="cpu", seed=0):
+    """One token per sequence for decode step ``step``: x, delta, z: (batch, dim);
+    B, C: (batch, N), in the io dtype."""
+    g = _gen(device, seed * 1000003 + 17 * step + 1)
+    shp = (w.batch, w.dim)
+    x = torch.randn(shp, generator=g, device=device)
+    delta = torch.randn(shp, generator=g, device=device) * w.delta_std
+    B = torch.randn((w.batch, w.dstate), generator=g, device=device)
+    C = torch.randn((w.batch, w.dstate), generator=g, device=device)
+    z = torch.randn(shp, generator=g, device=device) if w.gate else None
+    io = w.torch_io
+    return {"x": x.to(io), "delta": delta.to(io), "B": B.to(io), "C": C.to(io),
+            "z": None if z is None else z.to(io)}
+
+
+def to_f64_numpy(t):
+    """Exact widening of a (possibly bf16) tensor to a float64 numpy array."""
+    if t is None:
+        return None
+    return t.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,89 @@
+"""CPU test: the pins are sharp enough to catch plausible mistakes in the oracle.
+
+Each mutation below is a small, plausible slip (a dropped term, a wrong sign,
+a wrong index, a transposed operand, an off-by-one in time). The test applies
+it to a copy of ``oracle/ssm_oracle.c`` in a temporary directory, compiles the
+copy, runs every pin against it in a child process (a mutant may index badly,
+so it must not share this process), and requires at least one pin to fail
+(a crash does not count: the pins themselves must reject the mutant).
+The real oracle source is never modified.
+"""
+import json
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+from oracle.oracle import ORACLE_SRC, build_oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, exact text in ssm_oracle.c, replacement)
+MUTATIONS = [
+    ("softplus_pos_branch", "if (u > 0.0) return u + log1p(exp(-u));", "if (u > 0.0) return u;"),
+    ("softplus_neg_branch", "return log1p(exp(u));", "return exp(u);"),
+    ("euler_decay", "double abar = exp(Delta * A_d[n]);", "double abar = 1.0 + Delta * A_d[n];"),
+    ("bbar_without_delta", "bbar = Delta * B_t[n];", "bbar = B_t[n];"),
+    ("no_decay", "h[n] = abar * h[n] + bbar * x;", "h[n] = h[n] + bbar * x;"),
+    ("readout_with_B", "y += C_t[n] * h[n];", "y += B_t[n] * h[n];"),
+    ("drop_D", "if (D_d) y += (*D_d) * x;", ""),
+    ("drop_gate", "if (z) y *= silu(*z);", ""),
+    ("drop_bias", "double Delta = softplus(delta_raw + bias);", "double Delta = softplus(delta_raw);"),
+    ("A_row_index", "A + d * dstate,\n                          B + j", "A + d,\n                          B + j"),
+    ("nonzero_init", "h0[(b * dim + d) * dstate + n] : 0.0;", "h0[(b * dim + d) * dstate + n] : 1.0;"),
+    ("BC_time_off_by_one", "int64_t j = (b * seqlen + t) * dstate;",
+     "int64_t j = (b * seqlen + (t > 0 ? t - 1 : t)) * dstate;"),
+    ("sigmoid_sign", "return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    ("readout_before_update", "h[n] = abar * h[n] + bbar * x;\n    y += C_t[n] * h[n];",
+     "y += C_t[n] * h[n];\n    h[n] = abar * h[n] + bbar * x;"),
+    ("gate_before_D", "if (D_d) y += (*D_d) * x;\n  if (z) y *= silu(*z);",
+     "if (z) y *= silu(*z);\n  if (D_d) y += (*D_d) * x;"),
+    ("zoh_sign", "bbar = (abar - 1.0) / A_d[n] * B_t[n];", "bbar = (1.0 - abar) / A_d[n] * B_t[n];"),
+    ("decode_state_row", "out[i] = row_step(dstate, state + i * dstate",
+     "out[i] = row_step(dstate, state + d * dstate"),
+    ("decode_BC_swap", "B + b * dstate, C + b * dstate", "C + b * dstate, B + b * dstate"),
+    ("last_state_layout", "last_state[(b * dim + d) * dstate + n] = h[n];",
+     "last_state[(d * batch + b) * dstate + n] = h[n];"),
+    ("x_layout", "int64_t i = (b * seqlen + t) * dim + d;   /* (b, t, d) */",
+     "int64_t i = (t * batch + b) * dim + d;"),
+    ("decay_uses_bias_free_delta", "double abar = exp(Delta * A_d[n]);",
+     "double abar = exp(softplus(delta_raw) * A_d[n]);"),
+]
+
+RUNNER = textwrap.dedent("""
+    import json, sys
+    sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+    from oracle.oracle import Oracle
+    import pins
+    orc = Oracle({lib!r})
+    failed = []
+    for p in pins.ALL_PINS:
+        try:
+            p(orc)
+        except Exception as e:  # AssertionError, or a rejected call
+            failed.append(p.__name__)
+    print(json.dumps(failed))
+""")
+
+
+def test_mutation_list_applies_once():
+    src = open(ORACLE_SRC).read()
+    for name, old, new in MUTATIONS:
+        assert src.count(old) == 1, f"mutation {name}: pattern occurs {src.count(old)} times"
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1
+    mut_src = tmp_path / "ssm_oracle_mutant.c"
+    mut_src.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    build_oracle(str(mut_src), str(lib))
+    code = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=str(lib))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, f"mutant {name} crashed instead of failing a pin:\n{r.stderr[-2000:]}"
+    failed = json.loads(r.stdout.strip().splitlines()[-1])
+    assert failed, f"mutant {name} passed every pin"
