@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+One step = one full-sequence scan (mamba_scan_fwd) of the Mamba-2.8B-shaped
+prefill layer: batch 8, 5,120 channels, 2,048 tokens, 16 states, bf16 inputs,
+fp32 state, with bias, softplus, D skip and silu(z) gate. Inputs are seeded
+synthetic tensors already resident in HBM; the timed region holds exactly
+--steps calls bracketed by device synchronisation.
+
+Prints one JSON line. `value` is elem-steps/s (batch * L * channels per
+second). `roofline` relates the scan kernel's algorithmic HBM bytes per
+launch (every input read once, y and the final state written once) to its
+average launch time measured with HIP events on the launch stream.
+`cpu_baseline` is the fp64 oracle timed on this host on the same workload.
+The decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32 state) is
+measured in the same run and reported under `decode`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+METRIC = "scan fwd: (batch·L·D_inner) elem-steps/s + achieved HBM GB/s (% of peak)"
+
+
+def scan_bytes(w) -> int:
+    """Algorithmic HBM bytes of one scan: x, Delta_raw, z read and y written
+    (io dtype, once per element), B and C read once per token, A, D and bias
+    read once per channel, the fp32 final state written once."""
+    eb = 2 if w.io == "bf16" else 4
+    elems = w.batch * w.seqlen * w.dim
+    io_tensors = 3 if w.gate else 2
+    return (elems * eb * (io_tensors + 1) + 2 * w.batch * w.seqlen * w.dstate * eb
+            + w.dim * w.dstate * 4 + 2 * w.dim * 4 + w.batch * w.dim * w.dstate * 4)
+
+
+def decode_bytes(w) -> int:
+    """Per decode step: the fp32 state read and written, x, Delta_raw, z read,
+    y written, B and C per sequence, A, D and bias per channel."""
+    eb = 2 if w.io == "bf16" else 4
+    rows = w.batch * w.dim
+    return (2 * rows * w.dstate * 4 + rows * eb * 4 + 2 * w.batch * w.dstate * eb
+            + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+
+
+def time_calls(fn, n, stream):
+    """Run fn n times on `stream`, timing each call with HIP events recorded on
+    that stream. Returns the list of per-call milliseconds."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+    stream.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, inp, nthreads):
+    """The fp64 oracle on the whole workload, on this host's cores."""
+    import numpy as np  # noqa: F401
+    from oracle import default_oracle
+    from selective_state_space_56_amd.workloads import to_f64_numpy
+    orc = default_oracle()
+    args = [to_f64_numpy(inp[k]) for k in ("x", "delta", "A", "B", "C")]
+    kw = {k: to_f64_numpy(inp[k]) for k in ("D", "z", "delta_bias")}
+    t0 = time.perf_counter()
+    orc.scan(*args, **kw, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": w.elem_steps / dt, "unit": "elem-steps/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"whole workload ({w.batch}x{w.seqlen}x{w.dim}, N={w.dstate}), fp64, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2p8b_prefill")
+    ap.add_argument("--segments", type=int, default=0, help="force time segments (0 = library plan)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows are independent, so batch/channel sharding would need no communication; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_56_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from selective_state_space_56_amd.build import build
+        build()
+    from selective_state_space_56_amd import scan_fwd, state_update
+    from selective_state_space_56_amd.workloads import (WORKLOADS, make_decode_state,
+                                                        make_decode_token, make_params,
+                                                        make_scan_inputs)
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    inp = make_scan_inputs(w, device=dev)
+    out = torch.empty((w.batch, w.seqlen, w.dim), dtype=w.torch_io, device=dev)
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def step():
+        scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                 delta_bias=inp["delta_bias"], out=out, last_state=last, segments=args.segments)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per_call = time_calls(step, args.steps, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    value = w.elem_steps * args.steps / elapsed
+    kern_ms = sum(per_call) / len(per_call)
+    nbytes = scan_bytes(w)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    segs = binding.workspace_size(w.batch, w.seqlen, w.dim, w.dstate, w.torch_io, args.segments)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elem-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes of a Mamba-2.8B layer)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.dim,
+                   "d_state": w.dstate, "io": w.io, "state": "f32", "gate": w.gate,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "mamba_scan_fwd (all launches of one call)",
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": kern_ms,
+                     "min_launch_ms": min(per_call), "workspace_bytes": segs},
+    }
+
+    if not args.no_decode:
+        wd = WORKLOADS["decode_4096"]
+        params = make_params(wd, device=dev)
+        state = make_decode_state(wd, device=dev)
+        toks = [make_decode_token(wd, s, device=dev) for s in range(wd.decode_steps)]
+        outd = torch.empty((wd.batch, wd.dim), dtype=wd.torch_io, device=dev)
+        it = iter(range(10 ** 9))
+
+        def dstep():
+            t = toks[next(it) % wd.decode_steps]
+            state_update(state, t["x"], t["delta"], params["A"], t["B"], t["C"], D=params["D"],
+                         z=t["z"], delta_bias=params["delta_bias"], out=outd)
+
+        for _ in range(4):
+            dstep()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        dcalls = time_calls(dstep, wd.decode_steps, stream)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        dms = sum(dcalls) / len(dcalls)
+        db = decode_bytes(wd)
+        rec["decode"] = {
+            "workload": wd.name, "steps": wd.decode_steps, "ms_total": dt * 1e3,
+            "value": wd.batch * wd.dim * wd.decode_steps / dt, "unit": "elem-steps/s",
+            "avg_launch_ms": dms,
+            "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_launch": db},
+        }
+        del toks, state
+
+    if not args.no_cpu_baseline:
+        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        rec["cpu_baseline"] = cpu_baseline(w, inp, nthreads)
+
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

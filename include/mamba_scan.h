@@ -1,0 +1,143 @@
+/*
+ * mamba_scan.h — C ABI of the gfx950 selective state-space scan (S6).
+ *
+ * The operation (per batch row b, channel d, state n; one independent SSM per
+ * channel with a D x N state per layer — "Mamba and selective state spaces,
+ * from first principles", section "A state space model"):
+ *
+ *   Delta_t  = softplus(delta[b,t,d] + delta_bias[d])
+ *              (section "Selection: B, C and Delta from the token")
+ *   Abar     = exp(Delta_t * A[d,n])
+ *              (sections "Discretisation: zero-order hold" and "Selection")
+ *   Bbar x   = Delta_t * B[b,t,n] * x[b,t,d]
+ *              (first-order Bbar, the form the page says the reference code
+ *               computes, section "Discretisation: zero-order hold")
+ *   h_t[n]   = Abar * h_{t-1}[n] + Bbar x,   h_{-1} = 0
+ *              (erikxu.me notes "Mamba: Linear-Time Sequence Modeling with
+ *               Selective State Spaces", section "State Space Models")
+ *   y_t      = (sum_n C[b,t,n] h_t[n] + D[d] x[b,t,d]) * silu(z[b,t,d])
+ *              (D term: "State space models and Mamba", section "One system,
+ *               two views"; gate: "Mamba and selective state spaces", section
+ *               "The Mamba block")
+ *
+ * The full-sequence call loads the inputs once, keeps every state on chip and
+ * writes back only y of shape (batch, L, D) and the final state ("Mamba and
+ * selective state spaces", section "The hardware-aware scan"). The decode call
+ * advances a resident fp32 state by one token (erikxu.me notes, "State Space
+ * Models": constant work per generated token).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *    by the caller, dense and row-major in the shapes given below. The library
+ *    never allocates, frees or retains them.
+ *  - io tensors (x, delta, z, B, C, out) are float32 (MAMBA_F32) or bfloat16
+ *    bit patterns (MAMBA_BF16, 2 bytes each); A, D, delta_bias, state and
+ *    last_state are always float32. All arithmetic is float32.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously on it; nothing synchronises the host.
+ *  - Argument validation is synchronous and happens before any HIP call: a
+ *    non-OK status means nothing was enqueued. MAMBA_ERR_HIP reports a launch
+ *    failure; faults during execution surface at the caller's next
+ *    synchronisation. A thread-local message for the last non-OK status is
+ *    returned by mamba_last_error(). No C++ exception crosses the ABI.
+ *  - Calls on different streams may run concurrently as long as their output
+ *    buffers (and workspaces) do not overlap.
+ *  - Non-finite inputs are not checked; they propagate.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mamba_status {
+  MAMBA_OK = 0,
+  MAMBA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, overlap, ... */
+  MAMBA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement   */
+  MAMBA_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed     */
+} mamba_status;
+
+typedef enum mamba_dtype {
+  MAMBA_F32 = 0,
+  MAMBA_BF16 = 1
+} mamba_dtype;
+
+/*
+ * Problem sizes. dstate (N) must be 1, 2, 4, 8 or 16.
+ * flags: for mamba_scan_fwd, bits 0-15 force the number of time segments the
+ * sequence is cut into (0 = the library's choice; results agree to rounding
+ * for any value, and the workspace size depends on it); all other bits, and
+ * every bit for mamba_state_update, must be 0.
+ */
+typedef struct mamba_scan_desc {
+  int64_t batch;   /* >= 0                                         */
+  int64_t seqlen;  /* L >= 0 (must be 1 for mamba_state_update)    */
+  int64_t dim;     /* D_inner channels >= 0                        */
+  int64_t dstate;  /* N                                            */
+  int32_t io_dtype;/* mamba_dtype of x, delta, z, B, C and out     */
+  uint32_t flags;  /* see above                                    */
+} mamba_scan_desc;
+
+/*
+ * Bytes of device workspace mamba_scan_fwd needs for this problem (0 when
+ * none). The amount depends only on the sizes in `desc`. Returns 0 for an
+ * invalid descriptor as well; mamba_scan_fwd reports the error.
+ */
+size_t mamba_scan_workspace_size(const mamba_scan_desc *desc);
+
+/*
+ * Full-sequence selective scan.
+ *   x, delta, z : (batch, seqlen, dim) io dtype. delta is Delta_raw, before the
+ *                 bias and the softplus. z may be NULL (no gate).
+ *   A           : (dim, dstate) float32.
+ *   B, C        : (batch, seqlen, dstate) io dtype, shared by all channels.
+ *   D           : (dim) float32 or NULL (no direct term).
+ *   delta_bias  : (dim) float32 or NULL (zero bias).
+ *   out         : (batch, seqlen, dim) io dtype, written.
+ *   last_state  : (batch, dim, dstate) float32 or NULL; receives h_{L-1}
+ *                 (zeros when seqlen == 0).
+ *   workspace   : device scratch of at least mamba_scan_workspace_size(desc)
+ *                 bytes, 256-byte aligned (may be NULL when that size is 0).
+ *                 Its contents on entry are ignored; calls running
+ *                 concurrently must not share it.
+ * out and last_state must not overlap any input or each other.
+ */
+mamba_status mamba_scan_fwd(const mamba_scan_desc *desc, const void *x,
+                            const void *delta, const float *A, const void *B,
+                            const void *C, const float *D, const void *z,
+                            const float *delta_bias, void *out,
+                            float *last_state, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token for every sequence, against a resident state
+ * (desc->seqlen must be 1).
+ *   state       : (batch, dim, dstate) float32, read and overwritten in place
+ *                 with the state after this token.
+ *   x, delta, z : (batch, dim) io dtype (z may be NULL).
+ *   B, C        : (batch, dstate) io dtype.
+ *   A, D, delta_bias : as in mamba_scan_fwd.
+ *   out         : (batch, dim) io dtype, written; must not overlap any input.
+ */
+mamba_status mamba_state_update(const mamba_scan_desc *desc, float *state,
+                                const void *x, const void *delta,
+                                const float *A, const void *B, const void *C,
+                                const float *D, const void *z,
+                                const float *delta_bias, void *out,
+                                void *stream);
+
+/* Static name of a status code ("MAMBA_OK", ...). */
+const char *mamba_status_string(int status);
+
+/* Detail for the last non-OK status returned on this thread ("" if none). */
+const char *mamba_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

@@ -1,0 +1,181 @@
+"""ctypes binding of ``libmamba_scan.so`` (C ABI in ``include/mamba_scan.h``).
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch's caching allocator, and the current HIP stream. Every step of the
+computation runs in the library's kernels; there is no other code path, and a
+missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmamba_scan.so")
+
+MAMBA_OK = 0
+MAMBA_F32 = 0
+MAMBA_BF16 = 1
+_IO = {torch.float32: MAMBA_F32, torch.bfloat16: MAMBA_BF16}
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the native library once. Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first "
+                               "(python -m selective_state_space_56_amd.build)")
+        lib = ctypes.CDLL(path)
+        vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+        lib.mamba_scan_workspace_size.restype = sz
+        lib.mamba_scan_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        lib.mamba_scan_fwd.restype = ctypes.c_int
+        lib.mamba_scan_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, vp, fp,
+                                       vp, sz, vp]
+        lib.mamba_state_update.restype = ctypes.c_int
+        lib.mamba_state_update.argtypes = [ctypes.POINTER(Desc), fp, vp, vp, fp, vp, vp, fp, vp, fp,
+                                           vp, vp]
+        lib.mamba_status_string.restype = ctypes.c_char_p
+        lib.mamba_status_string.argtypes = [ctypes.c_int]
+        lib.mamba_last_error.restype = ctypes.c_char_p
+        lib.mamba_last_error.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _check(lib, status: int):
+    if status != MAMBA_OK:
+        name = lib.mamba_status_string(status).decode()
+        raise MambaScanError(status, f"{name}: {lib.mamba_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(batch, seqlen, dim, dstate, io_dtype=torch.bfloat16, segments=0) -> int:
+    lib = load_library()
+    d = Desc(batch, seqlen, dim, dstate, _IO[io_dtype], segments)
+    return int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None, last_state=None,
+             return_last_state=True, segments=0):
+    """Selective scan over full sequences.
+
+    x, delta (Delta_raw), z: (batch, L, dim) float32 or bfloat16 on a GPU;
+    A: (dim, N) float32; B, C: (batch, L, N) in x's dtype; D, delta_bias:
+    (dim,) float32 or None. Returns (out, last_state) where out is
+    (batch, L, dim) in x's dtype and last_state (batch, dim, N) float32 (None
+    if not requested). ``segments`` > 0 forces the number of time segments.
+    """
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, dim) and A (dim, N)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd runs on a GPU tensor")
+    io = x.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(delta, "delta", (batch, L, dim), io, dev)
+    _need(z, "z", (batch, L, dim), io, dev)
+    _need(B, "B", (batch, L, N), io, dev)
+    _need(C, "C", (batch, L, N), io, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _need(x, "x", (batch, L, dim), io, dev)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=io, device=dev)
+    _need(out, "out", (batch, L, dim), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    d = Desc(batch, L, dim, N, _IO[io], int(segments))
+    ws_bytes = int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.mamba_scan_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out), _ptr(last_state),
+                            _ptr(ws), ctypes.c_size_t(ws_bytes), _stream(dev))
+    _check(lib, st)
+    return out, last_state
+
+
+def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None):
+    """One decode token: advances ``state`` (batch, dim, N) float32 in place and
+    returns out (batch, dim). x, delta, z: (batch, dim); B, C: (batch, N)."""
+    lib = load_library()
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x must be (batch, dim) and A (dim, N)")
+    batch, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("state_update runs on a GPU tensor")
+    io = x.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(state, "state", (batch, dim, N), torch.float32, dev)
+    _need(delta, "delta", (batch, dim), io, dev)
+    _need(z, "z", (batch, dim), io, dev)
+    _need(B, "B", (batch, N), io, dev)
+    _need(C, "C", (batch, N), io, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    _need(out, "out", (batch, dim), io, dev)
+    d = Desc(batch, 1, dim, N, _IO[io], 0)
+    st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
+                                _stream(dev))
+    _check(lib, st)
+    return out

@@ -1,0 +1,256 @@
+// C ABI of the selective scan library: argument validation, planning and
+// dispatch to the HIP kernels. See include/mamba_scan.h for the contract.
+#include "mamba_scan.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mamba_status fail(mamba_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mamba_status ok() {
+  g_last_error.clear();
+  return MAMBA_OK;
+}
+
+bool supported_dstate(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+size_t io_bytes(int32_t io) { return io == MAMBA_BF16 ? 2 : 4; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const auto a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Checks the descriptor fields common to both entry points.
+mamba_status check_desc(const mamba_scan_desc* d, const char* who) {
+  if (!d) return fail(MAMBA_ERR_INVALID_ARG, "%s: desc is NULL", who);
+  if (d->batch < 0 || d->seqlen < 0 || d->dim < 0)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: negative size (batch=%lld seqlen=%lld dim=%lld)", who,
+                (long long)d->batch, (long long)d->seqlen, (long long)d->dim);
+  if (d->io_dtype != MAMBA_F32 && d->io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: io_dtype %d is not MAMBA_F32 or MAMBA_BF16", who,
+                (int)d->io_dtype);
+  if (d->dstate < 1) return fail(MAMBA_ERR_INVALID_ARG, "%s: dstate %lld < 1", who, (long long)d->dstate);
+  if (!supported_dstate(d->dstate))
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: dstate %lld not supported (1, 2, 4, 8 or 16)", who,
+                (long long)d->dstate);
+  // Keep every element index and grid size well inside 63 and 32 bits.
+  const int64_t lim = int64_t(1) << 40;
+  if (d->batch > lim || d->seqlen > lim || d->dim > lim ||
+      (d->batch && d->dim && d->batch > (int64_t(1) << 31) / d->dim) ||
+      (d->batch * d->dim && d->seqlen > lim / (d->batch * d->dim)))
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: problem too large", who);
+  return MAMBA_OK;
+}
+
+int forced_segments(const mamba_scan_desc* d) { return static_cast<int>(d->flags & 0xffffu); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mamba_status_string(int s) {
+  switch (s) {
+    case MAMBA_OK: return "MAMBA_OK";
+    case MAMBA_ERR_INVALID_ARG: return "MAMBA_ERR_INVALID_ARG";
+    case MAMBA_ERR_UNSUPPORTED: return "MAMBA_ERR_UNSUPPORTED";
+    case MAMBA_ERR_HIP: return "MAMBA_ERR_HIP";
+    default: return "MAMBA_ERR_UNKNOWN";
+  }
+}
+
+const char* mamba_last_error(void) { return g_last_error.c_str(); }
+
+size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
+  if (check_desc(d, "mamba_scan_workspace_size") != MAMBA_OK) return 0;
+  if (d->flags & ~0xffffu) return 0;
+  return mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
+                          forced_segments(d))
+      .workspace_bytes;
+}
+
+mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void* delta,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias, void* out, float* last_state,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "mamba_scan_fwd";
+  mamba_status st = check_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  if (d->flags & ~0xffffu)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
+  const int64_t rows = d->batch * d->dim;
+  const int64_t tokens = d->batch * d->seqlen;
+  const int64_t elems = tokens * d->dim;
+  if (elems > 0) {
+    if (!x) return fail(MAMBA_ERR_INVALID_ARG, "%s: x is NULL", who);
+    if (!delta) return fail(MAMBA_ERR_INVALID_ARG, "%s: delta is NULL", who);
+    if (!A) return fail(MAMBA_ERR_INVALID_ARG, "%s: A is NULL", who);
+    if (!B) return fail(MAMBA_ERR_INVALID_ARG, "%s: B is NULL", who);
+    if (!C) return fail(MAMBA_ERR_INVALID_ARG, "%s: C is NULL", who);
+    if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
+  }
+  const mscan::ScanPlan plan =
+      mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate), forced_segments(d));
+  if (elems > 0 && plan.workspace_bytes > 0) {
+    if (!workspace)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who,
+                  plan.workspace_bytes);
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace has %zu bytes, %zu needed", who,
+                  workspace_bytes, plan.workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", who);
+  }
+  const size_t eb = io_bytes(d->io_dtype);
+  const size_t N = static_cast<size_t>(d->dstate);
+  const Span in[] = {
+      {"x", x, static_cast<size_t>(elems) * eb},
+      {"delta", delta, static_cast<size_t>(elems) * eb},
+      {"z", z, static_cast<size_t>(elems) * eb},
+      {"B", B, static_cast<size_t>(tokens) * N * eb},
+      {"C", C, static_cast<size_t>(tokens) * N * eb},
+      {"A", A, static_cast<size_t>(d->dim) * N * 4},
+      {"D", D, static_cast<size_t>(d->dim) * 4},
+      {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
+  };
+  const Span o_out{"out", out, static_cast<size_t>(elems) * eb};
+  const Span o_last{"last_state", last_state, static_cast<size_t>(rows) * N * 4};
+  const Span o_ws{"workspace", elems > 0 ? workspace : nullptr, plan.workspace_bytes};
+  for (const Span& s : in) {
+    if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
+    if (overlaps(o_last, s))
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: last_state overlaps %s", who, s.name);
+    if (overlaps(o_ws, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace overlaps %s", who, s.name);
+  }
+  if (overlaps(o_out, o_last)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps last_state", who);
+  if (overlaps(o_ws, o_out) || overlaps(o_ws, o_last))
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace overlaps an output", who);
+  const size_t align = eb;
+  for (const Span& s : {in[0], in[1], in[2], in[3], in[4], o_out})
+    if (s.p && reinterpret_cast<uintptr_t>(s.p) % align)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, align);
+  for (const void* p : {static_cast<const void*>(A), static_cast<const void*>(D),
+                        static_cast<const void*>(delta_bias), static_cast<const void*>(last_state)})
+    if (p && reinterpret_cast<uintptr_t>(p) % 4)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: an fp32 argument is not 4-byte aligned", who);
+
+  if (rows == 0 || (elems == 0 && !last_state)) return ok();
+
+  mscan::ScanProblem p;
+  p.x = x;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.bias = delta_bias;
+  p.out = out;
+  p.last_state = last_state;
+  p.batch = d->batch;
+  p.seqlen = d->seqlen;
+  p.dim = d->dim;
+  p.dstate = static_cast<int>(d->dstate);
+  p.io = d->io_dtype;
+  const hipError_t e = mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const void* x,
+                                const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, void* out,
+                                void* stream) {
+  const char* who = "mamba_state_update";
+  mamba_status st = check_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  if (d->flags != 0) return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0", who);
+  if (d->seqlen != 1)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
+  const int64_t rows = d->batch * d->dim;
+  if (rows == 0) return ok();
+  if (!state) return fail(MAMBA_ERR_INVALID_ARG, "%s: state is NULL", who);
+  if (!x) return fail(MAMBA_ERR_INVALID_ARG, "%s: x is NULL", who);
+  if (!delta) return fail(MAMBA_ERR_INVALID_ARG, "%s: delta is NULL", who);
+  if (!A) return fail(MAMBA_ERR_INVALID_ARG, "%s: A is NULL", who);
+  if (!B) return fail(MAMBA_ERR_INVALID_ARG, "%s: B is NULL", who);
+  if (!C) return fail(MAMBA_ERR_INVALID_ARG, "%s: C is NULL", who);
+  if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
+  const size_t eb = io_bytes(d->io_dtype);
+  const size_t N = static_cast<size_t>(d->dstate);
+  const Span in[] = {
+      {"x", x, static_cast<size_t>(rows) * eb},
+      {"delta", delta, static_cast<size_t>(rows) * eb},
+      {"z", z, static_cast<size_t>(rows) * eb},
+      {"B", B, static_cast<size_t>(d->batch) * N * eb},
+      {"C", C, static_cast<size_t>(d->batch) * N * eb},
+      {"A", A, static_cast<size_t>(d->dim) * N * 4},
+      {"D", D, static_cast<size_t>(d->dim) * 4},
+      {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
+  };
+  const Span o_state{"state", state, static_cast<size_t>(rows) * N * 4};
+  const Span o_out{"out", out, static_cast<size_t>(rows) * eb};
+  for (const Span& s : in) {
+    if (overlaps(o_state, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: state overlaps %s", who, s.name);
+    if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
+  }
+  if (overlaps(o_out, o_state)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps state", who);
+  const size_t state_align = N >= 4 ? 16 : 4;
+  if (reinterpret_cast<uintptr_t>(state) % state_align)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: state is not %zu-byte aligned", who, state_align);
+  for (const Span& s : {in[0], in[1], in[2], in[3], in[4], o_out})
+    if (s.p && reinterpret_cast<uintptr_t>(s.p) % eb)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, eb);
+  for (const void* p : {static_cast<const void*>(A), static_cast<const void*>(D),
+                        static_cast<const void*>(delta_bias)})
+    if (p && reinterpret_cast<uintptr_t>(p) % 4)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: an fp32 argument is not 4-byte aligned", who);
+
+  mscan::DecodeProblem p;
+  p.state = state;
+  p.x = x;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.bias = delta_bias;
+  p.out = out;
+  p.batch = d->batch;
+  p.dim = d->dim;
+  p.dstate = static_cast<int>(d->dstate);
+  p.io = d->io_dtype;
+  const hipError_t e = mscan::launch_state_update(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Device-side element helpers shared by the scan and decode kernels (gfx950).
+//
+// Transcendentals use the gfx950 hardware instructions directly
+// (v_exp_f32 = 2^x, v_log_f32 = log2 x, v_rcp_f32 = 1/x); softplus and silu are
+// written from their definitions on top of them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// Storage types for the io tensors.
+struct F32Io {
+  using raw = float;
+  static __device__ __forceinline__ float load(const raw* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(raw v) { return v; }
+  static __device__ __forceinline__ raw from_f32(float v) { return v; }
+};
+
+struct Bf16Io {
+  using raw = uint16_t;
+  static __device__ __forceinline__ float to_f32(raw v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  static __device__ __forceinline__ float load(const raw* p) { return to_f32(*p); }
+  // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  static __device__ __forceinline__ raw from_f32(float v) {
+    __bf16 b = static_cast<__bf16>(v);
+    return __builtin_bit_cast(uint16_t, b);
+  }
+};
+
+// softplus(u) = log(1 + e^u).
+// w = 1 + e^u is rounded; for w in [1, 2) the rounding error r = e^u - (w - 1)
+// is exact (w - 1 is exact there) and log(1 + e^u) = log(w) + r / w to first
+// order, with 1/w ~ 2 - w. For w >= 2 the rounding of w moves log(w) by less
+// than 2^-24 relative, so no correction is applied. Above u = 20 the result is
+// u to within e^-20 (and e^u may overflow), so u is returned.
+__device__ __forceinline__ float softplus_f(float u) {
+  float e = hw_exp2(u * kLog2e);
+  float w = 1.0f + e;
+  float r = e - (w - 1.0f);
+  float inv_w = fmaxf(2.0f - w, 0.0f);
+  float s = fmaf(hw_log2(w), kLn2, r * inv_w);
+  return u > 20.0f ? u : s;
+}
+
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v). For v -> -inf, e^-v = inf and the
+// reciprocal gives 0.
+__device__ __forceinline__ float silu_f(float v) {
+  return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e));
+}
+
+}  // namespace mscan

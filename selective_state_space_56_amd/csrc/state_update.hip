@@ -1,0 +1,142 @@
+// One-token decode (state update) on gfx950.
+//
+// Every sequence carries a D x N fp32 state that stays resident in HBM; one
+// token advances it by exactly one step of the scan's recurrence and emits
+// that step's output (erikxu.me notes "Mamba: Linear-Time Sequence Modeling
+// with Selective State Spaces", section "State Space Models": constant work
+// per generated token; "Mamba and selective state spaces, from first
+// principles", section "A fixed state against a growing cache": decode is
+// bound by memory traffic).
+//
+// The kernel is a single streaming pass over the state: each row's N states
+// are split over N / 4 lanes that hold four consecutive states each, so one
+// wave64 reads and writes a contiguous run of 64 x 16 bytes with 16-byte
+// vector accesses. The per-row front-end (softplus, gate) is recomputed by
+// each lane of the row; the C read-out is summed across the row's lanes with
+// cross-lane shuffles.
+#include "device_math.h"
+#include "kernels.h"
+
+namespace mscan {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+struct DecodeKernelArgs {
+  float* state;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  void* out;
+  int64_t rows;  // batch * dim
+  int64_t dim;
+};
+
+template <int N, class IO>
+__global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a) {
+  using raw = typename IO::raw;
+  constexpr int SPL = N >= 4 ? 4 : N;  // states per lane
+  constexpr int LPR = N / SPL;         // lanes per row (1, 2 or 4; a power of 2)
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t row_raw = gid / LPR;
+  const int sub = static_cast<int>(gid % LPR);
+  const bool active = row_raw < a.rows;
+  // Inactive lanes of the last block mirror the last row so that the
+  // cross-lane sum below sees full lane groups; they store nothing.
+  const int64_t row = active ? row_raw : a.rows - 1;
+  const int64_t b = row / a.dim;
+  const int64_t d = row - b * a.dim;
+
+  const float xf = IO::load(static_cast<const raw*>(a.x) + row);
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float Delta = softplus_f(IO::load(static_cast<const raw*>(a.delta) + row) + bias);
+  const float dx = Delta * xf;
+
+  float* hp = a.state + row * N + sub * SPL;
+  float h[SPL];
+  if constexpr (SPL == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(hp);
+    h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) h[k] = hp[k];
+  }
+
+  const raw* Bt = static_cast<const raw*>(a.B) + b * N + sub * SPL;
+  const raw* Ct = static_cast<const raw*>(a.C) + b * N + sub * SPL;
+  const float* Ad = a.A + d * N + sub * SPL;
+  float y = 0.0f;
+#pragma unroll
+  for (int k = 0; k < SPL; ++k) {
+    const float abar = hw_exp2(Delta * (Ad[k] * kLog2e));
+    h[k] = fmaf(abar, h[k], dx * IO::load(Bt + k));
+    y = fmaf(IO::load(Ct + k), h[k], y);
+  }
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) y += __shfl_xor(y, off);
+
+  if (active) {
+    if constexpr (SPL == 4) {
+      *reinterpret_cast<float4*>(hp) = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) hp[k] = h[k];
+    }
+    if (sub == 0) {
+      if (a.D) y = fmaf(a.D[d], xf, y);
+      if (a.z) y *= silu_f(IO::load(static_cast<const raw*>(a.z) + row));
+      static_cast<raw*>(a.out)[row] = IO::from_f32(y);
+    }
+  }
+}
+
+template <int N, class IO>
+hipError_t launch_typed(const DecodeProblem& p, hipStream_t stream) {
+  constexpr int SPL = N >= 4 ? 4 : N;
+  constexpr int LPR = N / SPL;
+  DecodeKernelArgs a;
+  a.state = p.state;
+  a.x = p.x;
+  a.delta = p.delta;
+  a.A = p.A;
+  a.B = p.B;
+  a.C = p.C;
+  a.D = p.D;
+  a.z = p.z;
+  a.bias = p.bias;
+  a.out = p.out;
+  a.rows = p.batch * p.dim;
+  a.dim = p.dim;
+  const int64_t threads = a.rows * LPR;
+  const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL((state_update_kernel<N, IO>), grid, dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class IO>
+hipError_t dispatch_n(const DecodeProblem& p, hipStream_t st) {
+  switch (p.dstate) {
+    case 1: return launch_typed<1, IO>(p, st);
+    case 2: return launch_typed<2, IO>(p, st);
+    case 4: return launch_typed<4, IO>(p, st);
+    case 8: return launch_typed<8, IO>(p, st);
+    case 16: return launch_typed<16, IO>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_state_update(const DecodeProblem& p, hipStream_t stream) {
+  if (p.batch == 0 || p.dim == 0) return hipSuccess;
+  if (p.io == kIoBf16) return dispatch_n<Bf16Io>(p, stream);
+  return dispatch_n<F32Io>(p, stream);
+}
+
+}  // namespace mscan

@@ -1,0 +1,65 @@
+"""Helpers for the GPU parity tests: running the HIP path through the C ABI
+binding and the fp64 oracle on the same seeded inputs, and the error metric.
+
+Error metric (the pages fix no definition of "relative error"; outputs gated
+by silu(z) have many entries near zero, where an elementwise relative error
+means nothing): err = max_i |g_i - r_i| / (|r_i| + rms(r)), computed per
+tensor. Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32
+state, both against the oracle run on the exact (bf16-rounded) inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from selective_state_space_56_amd import scan_fwd, state_update
+from selective_state_space_56_amd.workloads import to_f64_numpy
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def norm_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    denom = np.abs(ref) + rms
+    if rms == 0.0:
+        return float(np.max(np.abs(got - ref)))
+    return float(np.max(np.abs(got - ref) / denom))
+
+
+def to_dev(inp, device="cuda"):
+    return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
+
+
+def gpu_scan(inp, segments=0, with_D=True, with_z=True, with_bias=True):
+    out, last = scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                         D=inp["D"] if with_D else None, z=inp["z"] if with_z else None,
+                         delta_bias=inp["delta_bias"] if with_bias else None, segments=segments)
+    torch.cuda.synchronize()
+    return out, last
+
+
+def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=True, nthreads=None):
+    """Run the oracle on the exact stored inputs (optionally only on a subset
+    of channels; rows are independent, so that is the same computation)."""
+    def sl(t, dim_axis):
+        if t is None:
+            return None
+        a = to_f64_numpy(t)
+        if channels is not None:
+            a = np.take(a, channels, axis=dim_axis)
+        return a
+    A = sl(inp["A"], 0)
+    return orc.scan(sl(inp["x"], 2), sl(inp["delta"], 2), A, to_f64_numpy(inp["B"]),
+                    to_f64_numpy(inp["C"]), D=sl(inp["D"], 0) if with_D else None,
+                    z=sl(inp["z"], 2) if with_z else None,
+                    delta_bias=sl(inp["delta_bias"], 0) if with_bias else None, nthreads=nthreads)
+
+
+def gpu_decode(state, tok, params):
+    return state_update(state, tok["x"], tok["delta"], params["A"], tok["B"], tok["C"],
+                        D=params["D"], z=tok["z"], delta_bias=params["delta_bias"])

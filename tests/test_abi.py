@@ -1,0 +1,161 @@
+"""CPU tests of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments synchronously, before any HIP call
+(so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_56_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from selective_state_space_56_amd.build import build
+        build()
+    return bd.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_state_update",
+                          "mamba_status_string", "mamba_last_error"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.mamba_status_string(0) == b"MAMBA_OK"
+    assert lib.mamba_status_string(1) == b"MAMBA_ERR_INVALID_ARG"
+    assert lib.mamba_status_string(2) == b"MAMBA_ERR_UNSUPPORTED"
+    assert lib.mamba_status_string(3) == b"MAMBA_ERR_HIP"
+    assert lib.mamba_status_string(99) == b"MAMBA_ERR_UNKNOWN"
+
+
+def P(k):
+    """Distinct fake device addresses, 4 KiB apart (aligned, non-overlapping
+    for the tiny sizes used here)."""
+    return ctypes.c_void_p(FAKE + 0x100000 * k)
+
+
+def scan(lib, desc, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, out=9, last=10, ws=None,
+         ws_bytes=0):
+    args = [x, delta, A, B, C, D, z, bias, out, last]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
+    return lib.mamba_scan_fwd(None if desc is None else ctypes.byref(desc), *ptrs, w,
+                              ctypes.c_size_t(ws_bytes), None)
+
+
+def upd(lib, desc, state=11, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, out=9):
+    args = [state, x, delta, A, B, C, D, z, bias, out]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    return lib.mamba_state_update(None if desc is None else ctypes.byref(desc), *ptrs, None)
+
+
+def D_(batch=2, seqlen=8, dim=16, dstate=16, io=1, flags=0):
+    return bd.Desc(batch, seqlen, dim, dstate, io, flags)
+
+
+def err(lib):
+    return lib.mamba_last_error().decode()
+
+
+def test_scan_rejects_bad_descriptors(lib):
+    assert scan(lib, None) == INVALID
+    assert "desc is NULL" in err(lib)
+    assert scan(lib, D_(batch=-1)) == INVALID
+    assert scan(lib, D_(seqlen=-3)) == INVALID
+    assert scan(lib, D_(dim=-2)) == INVALID
+    assert scan(lib, D_(io=7)) == INVALID
+    assert scan(lib, D_(dstate=0)) == INVALID
+    for n in (3, 5, 32, 64):
+        assert scan(lib, D_(dstate=n)) == UNSUPPORTED
+        assert "dstate" in err(lib)
+    assert scan(lib, D_(flags=1 << 16)) == INVALID
+    assert scan(lib, D_(batch=1 << 20, dim=1 << 20)) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("missing", ["x", "delta", "A", "B", "C", "out"])
+def test_scan_rejects_null_required(lib, missing):
+    assert scan(lib, D_(), **{missing: None}) == INVALID
+    assert missing in err(lib)
+
+
+def test_scan_rejects_overlap_and_alignment(lib):
+    assert scan(lib, D_(), out=1) == INVALID               # out == x
+    assert "out overlaps x" in err(lib)
+    assert scan(lib, D_(), last=4) == INVALID              # last_state == B
+    assert scan(lib, D_(), last=9) == INVALID              # last_state == out
+    odd = ctypes.c_void_p(FAKE + 0x100000 + 1)
+    assert scan(lib, D_(), x=odd) == INVALID
+    assert "aligned" in err(lib)
+    odd4 = ctypes.c_void_p(FAKE + 0x100000 * 3 + 2)
+    assert scan(lib, D_(), A=odd4) == INVALID
+
+
+def test_scan_workspace_contract(lib):
+    # forcing 4 time segments needs a workspace; passing none or too little fails
+    d = D_(batch=1, seqlen=64, dim=16, flags=4)
+    need = lib.mamba_scan_workspace_size(ctypes.byref(d))
+    assert need >= 3 * 16 * 17 * 4 and need % 256 == 0
+    assert scan(lib, d) == INVALID
+    assert "workspace" in err(lib)
+    assert scan(lib, d, ws=20, ws_bytes=need - 1) == INVALID
+    mis = ctypes.c_void_p(FAKE + 0x100000 * 20 + 64)
+    assert scan(lib, d, ws=mis, ws_bytes=need) == INVALID
+    assert scan(lib, d, ws=1, ws_bytes=need) == INVALID   # workspace overlaps x
+    # small problems need none; invalid descriptors report 0
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(batch=64, seqlen=256, dim=4096))) == 0
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(dstate=3))) == 0
+    assert lib.mamba_scan_workspace_size(None) == 0
+
+
+def test_workspace_size_is_deterministic(lib):
+    for shape in [(1, 131072, 5120), (2, 2048, 1536), (8, 2048, 5120), (1, 256, 64)]:
+        d = D_(batch=shape[0], seqlen=shape[1], dim=shape[2])
+        a = lib.mamba_scan_workspace_size(ctypes.byref(d))
+        b = lib.mamba_scan_workspace_size(ctypes.byref(d))
+        assert a == b and a % 256 == 0
+
+
+def test_scan_empty_problems_are_noops(lib):
+    # no rows: nothing to do, no pointer needed, no HIP call
+    assert scan(lib, D_(batch=0), x=None, delta=None, A=None, B=None, C=None, out=None) == 0
+    assert scan(lib, D_(dim=0), x=None, delta=None, A=None, B=None, C=None, out=None) == 0
+    # zero-length sequence without a final state: nothing to write
+    assert scan(lib, D_(seqlen=0), x=None, delta=None, A=None, B=None, C=None, out=None,
+                last=None) == 0
+    assert err(lib) == ""
+
+
+def test_state_update_validation(lib):
+    assert upd(lib, None) == INVALID
+    assert upd(lib, D_(seqlen=2)) == INVALID
+    assert "seqlen must be 1" in err(lib)
+    assert upd(lib, D_(seqlen=1, flags=1)) == INVALID
+    assert upd(lib, D_(seqlen=1, dstate=12)) == UNSUPPORTED
+    for missing in ["state", "x", "delta", "A", "B", "C", "out"]:
+        assert upd(lib, D_(seqlen=1), **{missing: None}) == INVALID, missing
+        assert missing in err(lib)
+    assert upd(lib, D_(seqlen=1), out=11) == INVALID       # out == state
+    assert upd(lib, D_(seqlen=1), state=1) == INVALID      # state == x
+    mis = ctypes.c_void_p(FAKE + 0x100000 * 11 + 8)        # 8-byte aligned only
+    assert upd(lib, D_(seqlen=1), state=mis) == INVALID
+    assert "16-byte" in err(lib)
+    assert upd(lib, D_(batch=0, seqlen=1), state=None, x=None, delta=None, A=None, B=None,
+               C=None, out=None) == 0

@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Small workloads are compared element by element in full;
+the full-size workloads run exactly as the benchmark launches them and are
+compared on sampled channels (rows are independent, so the oracle computes
+those channels exactly)."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import TOL, gpu_decode, gpu_scan, norm_err, oracle_scan, to_dev
+from selective_state_space_56_amd import scan_fwd, state_update
+from selective_state_space_56_amd.workloads import (WORKLOADS, make_decode_state, make_decode_token,
+                                                    make_params, make_scan_inputs, to_f64_numpy)
+
+pytestmark = pytest.mark.gpu
+
+NT = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_scan(orc, w, inp, segments=0, channels=None, tol=None, **kw):
+    tol = TOL[w.io] if tol is None else tol
+    out, last = gpu_scan(inp, segments=segments, **kw)
+    ref_y, ref_h = oracle_scan(orc, inp, channels=channels, nthreads=NT, **kw)
+    got_y = to_f64_numpy(out)
+    got_h = to_f64_numpy(last)
+    if channels is not None:
+        got_y = got_y[:, :, channels]
+        got_h = got_h[:, channels]
+    ey, eh = norm_err(got_y, ref_y), norm_err(got_h, ref_h)
+    _say(f"{w.name} {w.batch}x{w.seqlen}x{w.dim} N={w.dstate} seg={segments}: "
+         f"err(y)={ey:.3e} err(state)={eh:.3e} tol={tol:g}")
+    assert ey <= tol, f"y error {ey} > {tol}"
+    assert eh <= tol, f"state error {eh} > {tol}"
+    return ey, eh
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+def test_tiny_fp32_full(orc, dev):
+    w = WORKLOADS["tiny_fp32"]
+    _say(f"case {w.name}")
+    inp = to_dev(make_scan_inputs(w), dev)
+    _check_scan(orc, w, inp)
+
+
+def test_mamba130m_layer_full(orc, dev):
+    w = WORKLOADS["mamba130m_layer"]
+    _say(f"case {w.name}")
+    inp = to_dev(make_scan_inputs(w), dev)
+    ey, eh = _check_scan(orc, w, inp)
+    # bf16 rounding of y alone is 2^-9 relative; the fp32 state should be far tighter
+    assert eh < 1e-4
+
+
+@pytest.mark.parametrize("batch,L,dim,N,io,segments", [
+    (3, 1001, 300, 16, "bf16", 0),      # ragged tiles and tail
+    (3, 1001, 300, 16, "bf16", 7),
+    (1, 37, 1, 16, "f32", 0),           # one channel
+    (2, 1, 257, 16, "f32", 0),          # one step
+    (1, 513, 70, 1, "f32", 3),
+    (1, 513, 70, 2, "f32", 0),
+    (2, 300, 65, 4, "bf16", 5),
+    (1, 700, 129, 8, "f32", 2),
+    (1, 4096, 64, 16, "f32", 16),       # many segments, fp32 tolerance
+])
+def test_ragged_shapes(orc, dev, batch, L, dim, N, io, segments):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="ragged", batch=batch, seqlen=L, dim=dim,
+                                                 dstate=N, io=io)
+    _say(f"case ragged {batch}x{L}x{dim} N={N} {io} seg={segments}")
+    inp = to_dev(make_scan_inputs(w, seed=batch * 1000 + L), dev)
+    _check_scan(orc, w, inp, segments=segments)
+
+
+def test_optional_arguments_absent(orc, dev):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="noopt", batch=2, seqlen=300, dim=96)
+    _say("case optional arguments absent")
+    inp = to_dev(make_scan_inputs(w, seed=3), dev)
+    _check_scan(orc, w, inp, with_D=False, with_z=False, with_bias=False)
+    _check_scan(orc, w, inp, with_D=True, with_z=False, with_bias=False)
+
+
+def test_worked_example_on_gpu(dev):
+    """The scalar example of "State space models and Mamba" ("A worked
+    example"), run through the kernel with one state in fp32."""
+    import pins
+    g = pins.read_golden()
+    a, b = float(g["decay"][0]), float(g["input_weight"][0])
+    x = torch.tensor(g["inputs"], dtype=torch.float32, device=dev).view(1, 3, 1)
+    draw = torch.full((1, 3, 1), math.log(math.expm1(1.0)), dtype=torch.float32, device=dev)
+    A = torch.tensor([[math.log(a)]], dtype=torch.float32, device=dev)
+    B = torch.full((1, 3, 1), b, dtype=torch.float32, device=dev)
+    C = torch.ones((1, 3, 1), dtype=torch.float32, device=dev)
+    out, last = scan_fwd(x, draw, A, B, C)
+    np.testing.assert_allclose(out.cpu().numpy().ravel(), g["states"], rtol=2e-6, atol=1e-6)
+    Dd = torch.tensor([float(g["direct_term"][0])], device=dev)
+    out, _ = scan_fwd(x, draw, A, B, C, D=Dd)
+    np.testing.assert_allclose(out.cpu().numpy().ravel(), g["outputs_with_direct_term"], rtol=2e-6,
+                               atol=1e-6)
+
+
+def test_segment_invariance(orc, dev):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="seginv", batch=2, seqlen=2048, dim=384)
+    _say("case segment invariance")
+    inp = to_dev(make_scan_inputs(w, seed=5), dev)
+    outs = []
+    for s in (1, 2, 5, 16, 64):
+        _check_scan(orc, w, inp, segments=s)
+        outs.append(gpu_scan(inp, segments=s))
+    base_y = to_f64_numpy(outs[0][0])
+    for o, l in outs[1:]:
+        assert norm_err(to_f64_numpy(o), base_y) < 1e-2
+
+
+def test_zero_length_sequence(dev):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="empty", batch=2, seqlen=0, dim=40)
+    inp = to_dev(make_scan_inputs(w), dev)
+    last = torch.full((2, 40, 16), 7.0, device=dev)
+    out, last = scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                         z=inp["z"], delta_bias=inp["delta_bias"], last_state=last)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 0, 40)
+    assert torch.count_nonzero(last).item() == 0
+
+
+def test_run_twice_bitwise(dev):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="det", batch=2, seqlen=1024, dim=512)
+    inp = to_dev(make_scan_inputs(w, seed=9), dev)
+    for segs in (0, 4):
+        o1, l1 = gpu_scan(inp, segments=segs)
+        o2, l2 = gpu_scan(inp, segments=segs)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _sample_channels(dim, k, seed):
+    rng = np.random.default_rng(seed)
+    ch = np.unique(np.concatenate([[0, dim - 1, 255, 256], rng.choice(dim, k, replace=False)]))
+    return ch[ch < dim]
+
+
+def test_prefill_2p8b_full_size_sampled(orc, dev):
+    w = WORKLOADS["mamba2p8b_prefill"]
+    _say(f"case {w.name} (full size, sampled channels)")
+    inp = make_scan_inputs(w, device=dev)
+    _check_scan(orc, w, inp, channels=_sample_channels(w.dim, 60, 1))
+
+
+def test_long_context_full_size_sampled(orc, dev):
+    w = WORKLOADS["long_context_131k"]
+    _say(f"case {w.name} (full size, sampled channels)")
+    inp = make_scan_inputs(w, device=dev)
+    _check_scan(orc, w, inp, channels=_sample_channels(w.dim, 12, 2))
+
+
+def test_decode_full_size_sampled(orc, dev):
+    """64 consecutive one-token steps on 4096 sequences x 5120 channels x 16
+    states; the oracle follows sampled (sequence, channel) rows."""
+    w = WORKLOADS["decode_4096"]
+    _say(f"case {w.name} (full size, sampled rows)")
+    params = make_params(w, device=dev)
+    state = make_decode_state(w, device=dev)
+    bs = np.array([0, 1, 777, 2048, 4095])
+    ch = _sample_channels(w.dim, 24, 3)
+    ref_state = to_f64_numpy(state)[bs][:, ch]
+    A = to_f64_numpy(params["A"])[ch]
+    D = to_f64_numpy(params["D"])[ch]
+    bias = to_f64_numpy(params["delta_bias"])[ch]
+    worst_y = worst_h = 0.0
+    for step in range(w.decode_steps):
+        tok = make_decode_token(w, step, device=dev)
+        out = gpu_decode(state, tok, params)
+        t = {k: (None if v is None else to_f64_numpy(v)) for k, v in tok.items()}
+        ref_y, ref_state = orc.state_update(ref_state, t["x"][bs][:, ch], t["delta"][bs][:, ch], A,
+                                            t["B"][bs], t["C"][bs], D=D, z=t["z"][bs][:, ch],
+                                            delta_bias=bias, nthreads=NT)
+        worst_y = max(worst_y, norm_err(to_f64_numpy(out)[bs][:, ch], ref_y))
+    torch.cuda.synchronize()
+    worst_h = norm_err(to_f64_numpy(state)[bs][:, ch], ref_state)
+    _say(f"decode 64 steps: err(y)={worst_y:.3e} err(state)={worst_h:.3e}")
+    assert worst_y <= TOL["bf16"] and worst_h <= TOL["bf16"]
+    assert worst_h < 1e-4
+
+
+def test_decode_matches_scan(orc, dev):
+    """L one-token updates from a zero state reproduce the full-sequence scan
+    (erikxu.me notes, "State Space Models": the recurrent view), and prefill
+    followed by one decode step equals the scan of L + 1 tokens."""
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="dec", batch=3, seqlen=65, dim=200)
+    inp = to_dev(make_scan_inputs(w, seed=4), dev)
+    y_full, h_full = gpu_scan(inp)
+    state = torch.zeros((3, 200, 16), device=dev)
+    ys = []
+    for t in range(w.seqlen):
+        tok = {k: inp[k][:, t].contiguous() for k in ("x", "delta", "z", "B", "C")}
+        ys.append(gpu_decode(state, tok, inp).clone())
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    assert norm_err(to_f64_numpy(y_dec), to_f64_numpy(y_full)) < 1e-2
+    assert norm_err(to_f64_numpy(state), to_f64_numpy(h_full)) < 1e-5
+    # prefill(L-1) + one step
+    pre = {k: (v[:, :-1].contiguous() if k in ("x", "delta", "z", "B", "C") else v)
+           for k, v in inp.items()}
+    _, h_pre = gpu_scan(pre)
+    tok = {k: inp[k][:, -1].contiguous() for k in ("x", "delta", "z", "B", "C")}
+    y_last = gpu_decode(h_pre, tok, inp)
+    torch.cuda.synchronize()
+    assert norm_err(to_f64_numpy(y_last), to_f64_numpy(y_full[:, -1])) < 1e-2
+    assert norm_err(to_f64_numpy(h_pre), to_f64_numpy(h_full)) < 1e-5
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+def test_decode_small_vs_oracle(orc, dev, N):
+    w = WORKLOADS["decode_4096"].with_shape(name="dsmall", batch=5, dim=131, dstate=N, io="f32")
+    params = make_params(w, device=dev)
+    state = make_decode_state(w, device=dev)
+    ref_state = to_f64_numpy(state)
+    for step in range(6):
+        tok = make_decode_token(w, step, device=dev)
+        out = gpu_decode(state, tok, params)
+        t = {k: (None if v is None else to_f64_numpy(v)) for k, v in tok.items()}
+        ref_y, ref_state = orc.state_update(ref_state, t["x"], t["delta"], to_f64_numpy(params["A"]),
+                                            t["B"], t["C"], D=to_f64_numpy(params["D"]), z=t["z"],
+                                            delta_bias=to_f64_numpy(params["delta_bias"]))
+        assert norm_err(to_f64_numpy(out), ref_y) <= TOL["f32"]
+    torch.cuda.synchronize()
+    assert norm_err(to_f64_numpy(state), ref_state) <= TOL["f32"]
