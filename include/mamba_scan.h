@@ -104,7 +104,9 @@ size_t mamba_scan_workspace_size(const mamba_scan_desc *desc);
  *                 bytes, 256-byte aligned (may be NULL when that size is 0).
  *                 Its contents on entry are ignored; calls running
  *                 concurrently must not share it.
- * out and last_state must not overlap any input or each other.
+ * out and last_state must not overlap any input or each other. Alignment:
+ * io tensors to their element size, B and C to 4 bytes (2 for bf16 with
+ * dstate 1), fp32 tensors to 4 bytes.
  */
 mamba_status mamba_scan_fwd(const mamba_scan_desc *desc, const void *x,
                             const void *delta, const float *A, const void *B,

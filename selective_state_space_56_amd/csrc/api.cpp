@@ -61,6 +61,9 @@ mamba_status check_desc(const mamba_scan_desc* d, const char* who) {
                 (long long)d->dstate);
   // Keep every element index and grid size well inside 63 and 32 bits.
   const int64_t lim = int64_t(1) << 40;
+  // one time step of one tensor (dim * 4 bytes) must stay far below 2^31
+  if (d->dim > (int64_t(1) << 26))
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: dim %lld too large", who, (long long)d->dim);
   if (d->batch > lim || d->seqlen > lim || d->dim > lim ||
       (d->batch && d->dim && d->batch > (int64_t(1) << 31) / d->dim) ||
       (d->batch * d->dim && d->seqlen > lim / (d->batch * d->dim)))
@@ -151,9 +154,14 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
   if (overlaps(o_ws, o_out) || overlaps(o_ws, o_last))
     return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace overlaps an output", who);
   const size_t align = eb;
-  for (const Span& s : {in[0], in[1], in[2], in[3], in[4], o_out})
+  for (const Span& s : {in[0], in[1], in[2], o_out})
     if (s.p && reinterpret_cast<uintptr_t>(s.p) % align)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, align);
+  // B and C rows are read as 32-bit words (unless one bf16 state per step)
+  const size_t bc_align = (eb == 2 && N == 1) ? 2 : 4;
+  for (const Span& s : {in[3], in[4]})
+    if (s.p && reinterpret_cast<uintptr_t>(s.p) % bc_align)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, bc_align);
   for (const void* p : {static_cast<const void*>(A), static_cast<const void*>(D),
                         static_cast<const void*>(delta_bias), static_cast<const void*>(last_state)})
     if (p && reinterpret_cast<uintptr_t>(p) % 4)

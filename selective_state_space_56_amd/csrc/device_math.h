@@ -17,20 +17,68 @@ __device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
+// Read-only memory that every lane of a wave reads at the same address (B_t,
+// C_t): declaring it constant lets the compiler fetch it with scalar loads.
+template <class T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+
+template <class T>
+__device__ __forceinline__ const_ptr<T> as_const(const T* p) {
+  return (const_ptr<T>)(p);
+}
+
+// Buffer resource over a byte range that starts at `base` (wave-uniform). The
+// record count is the largest positive 32-bit value: a lane offset of
+// kOffNone is out of range, so its loads return 0 and its stores are dropped.
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  // 0x00020000: raw (untyped) buffer, dword data format, as CDNA expects
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           0x7fffffff, 0x00020000);
+}
+
 // Storage types for the io tensors.
+//   load_pair(p, k): elements 2k and 2k + 1 of a wave-uniform constant array,
+//   widened to fp32.
 struct F32Io {
   using raw = float;
+  static __device__ __forceinline__ void load_pair(const_ptr<float> p, int k, float& a, float& b) {
+    a = p[2 * k];
+    b = p[2 * k + 1];
+  }
   static __device__ __forceinline__ float load(const raw* p) { return *p; }
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void bstore(raw v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+  }
   static __device__ __forceinline__ float to_f32(raw v) { return v; }
   static __device__ __forceinline__ raw from_f32(float v) { return v; }
 };
 
 struct Bf16Io {
   using raw = uint16_t;
+  static __device__ __forceinline__ void load_pair(const_ptr<uint16_t> p, int k, float& a,
+                                                   float& b) {
+    const uint32_t w = ((const_ptr<uint32_t>)(p))[k];
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+  }
   static __device__ __forceinline__ float to_f32(raw v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
   }
   static __device__ __forceinline__ float load(const raw* p) { return to_f32(*p); }
+  static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+  static __device__ __forceinline__ void bstore(raw v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+  }
   // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
   static __device__ __forceinline__ raw from_f32(float v) {
     __bf16 b = static_cast<__bf16>(v);

@@ -120,7 +120,7 @@ def test_scan_workspace_contract(lib):
     assert scan(lib, d, ws=mis, ws_bytes=need) == INVALID
     assert scan(lib, d, ws=1, ws_bytes=need) == INVALID   # workspace overlaps x
     # small problems need none; invalid descriptors report 0
-    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(batch=64, seqlen=256, dim=4096))) == 0
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(batch=128, seqlen=256, dim=4096))) == 0
     assert lib.mamba_scan_workspace_size(ctypes.byref(D_(dstate=3))) == 0
     assert lib.mamba_scan_workspace_size(None) == 0
 
