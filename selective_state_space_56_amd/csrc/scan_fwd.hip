@@ -125,10 +125,13 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
 // LDS staging of one chunk of kChunk steps for the workgroup's channel tile:
 // x, Delta_raw and z as stored (raw io values) and B_t, C_t widened to fp32.
 // Two buffers: the next chunk is fetched while the current one is computed.
-template <int N, class IO>
+// With Y, the outputs y of a chunk are collected in LDS and written to HBM as
+// one tile at the start of the next chunk.
+template <int N, class IO, bool Y>
 struct __align__(16) Stage {
   typename IO::raw in[2][3][kChunk][kBlock];  // [buffer][x, Delta_raw, z][step][channel]
   float bc[2][kChunk][2 * N];                 // [buffer][step][B_0..B_{N-1}, C_0..C_{N-1}]
+  typename IO::raw yo[Y ? 2 : 1][Y ? kChunk : 1][kBlock];  // [buffer][step][channel]
 };
 
 using lds_void = __attribute__((address_space(3))) void;
@@ -160,6 +163,40 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, typename IO::
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, voff, 0, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, voff, 0, 0, 0);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Write the y tile of the chunk at step t0 from LDS to HBM: S bytes per lane
+// (the same pieces as dma_tile), or, with S == 0, each lane its own channel.
+template <class IO, int S>
+__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t r, const typename IO::raw* tile,
+                                           uint32_t row_bytes, uint32_t t0, uint32_t steps,
+                                           uint32_t valid_bytes, uint32_t voff) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const int tid = threadIdx.x;
+  if constexpr (S == 0) {
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+      if (t0 + j < steps) IO::bstore(tile[j * kBlock + tid], r, voff, (t0 + j) * row_bytes);
+  } else {
+    constexpr int kTileBytes = kChunk * kBlock * eb;
+    constexpr int kPerInstr = kBlock * S;
+#pragma unroll
+    for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
+      const int flat = (k * kBlock + tid) * S;
+      const int row = flat / (kBlock * eb), col = flat % (kBlock * eb);
+      const uint32_t t = t0 + row;
+      const uint32_t o = (t < steps && static_cast<uint32_t>(col + S) <= valid_bytes)
+                             ? t * row_bytes + col
+                             : kOffNone;
+      const char* src = reinterpret_cast<const char*>(tile) + flat;
+      if constexpr (S == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, o, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), r, o, 0, 0);
+    }
   }
 }
 
@@ -230,8 +267,13 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // CW: bytes per lane of each global-to-LDS copy: 16 when every channel tile
 // is a whole number of 16-byte pieces, 4 when of 32-bit words, and 0 for the
 // register-staged copy otherwise.
-template <int N, class IO, int MODE, bool GATE, int CW>
-__global__ __launch_bounds__(kBlock) void scan_segment_kernel(
+// Occupancy target: five 256-lane workgroups per CU (five waves per SIMD), so
+// the compiler keeps each lane within 102 vector registers instead of hoisting
+// loads of later steps.
+constexpr int kMinBlocksPerCU = 5;
+
+template <int N, class IO, int MODE, bool GATE, int CW, bool KSTRUCT>
+__global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
     const typename IO::raw* __restrict__ x, const typename IO::raw* __restrict__ delta,
     const float* __restrict__ A, const typename IO::raw* __restrict__ B,
     const typename IO::raw* __restrict__ C, const float* __restrict__ D,
@@ -244,7 +286,7 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(
   constexpr bool kC = MODE == kOutput;
   constexpr int kTileElems = kChunk * 2 * N;
   static_assert(kTileElems <= kBlock, "one B/C tile element per thread");
-  __shared__ Stage<N, IO> st;
+  __shared__ Stage<N, IO, MODE == kOutput> st;
 
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x / g.tiles;
@@ -297,7 +339,9 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(
   const raw* Cp = C + (b * g.seqlen + t_begin) * N;
   const int bci = tid % kTileElems;  // this thread's B/C tile element
 
-  const bool use_structured = __syncthreads_and(structured);
+  // Each launch covers either the S4D-Real-shaped tiles or the others; a
+  // workgroup of the other kind leaves at once (the whole group together).
+  if (__syncthreads_and(structured) != KSTRUCT) return;
   float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta (aggregate mode)
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
   // in registers on the register-staged path until land() writes them)
@@ -329,50 +373,65 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(
     wait_vmem();
     __syncthreads();
     const uint32_t n_chunks = (steps + kChunk - 1) / kChunk;
-    for (uint32_t c = 0; c < n_chunks; ++c) {
+    // One chunk: write out the previous chunk's y tile, start fetching the
+    // next chunk, run the steps, then land the next chunk's B/C and wait for
+    // its copies. MORE: not the last chunk (so all kChunk steps are valid).
+    auto chunk = [&](uint32_t c, auto more_tag, auto full_tag) {
+      constexpr bool MORE = decltype(more_tag)::value;
+      constexpr bool FULL = decltype(full_tag)::value;
       const int buf = c & 1;
       const uint32_t t0 = c * kChunk;
-      const bool more = c + 1 < n_chunks;
-      if (more) {
+      if (MODE == kOutput && c > 0)
+        store_tile<IO, CW>(ro, &st.yo[buf ^ 1][0][0], row_bytes, t0 - kChunk, steps, valid_bytes,
+                           voff);
+      if (MORE) {
         fetch(buf ^ 1, t0 + kChunk);
         bcv = bc_elem<N, IO>(Bp, Cp, t0 + kChunk, steps, bci);
       }
-      const uint32_t valid = more ? kChunk : steps - t0;
-      auto body = [&](auto structured_tag, auto full_tag) {
-        constexpr bool STRUCT = decltype(structured_tag)::value;
-        constexpr bool FULL = decltype(full_tag)::value;
-        FrontEnd fe = front_end<N, IO, MODE, GATE, STRUCT>(
-            st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][2][0][tid] : raw(0),
-            A2[0], bias);
+      const int valid = FULL ? kChunk : static_cast<int>(steps - t0);
+      FrontEnd fe = front_end<N, IO, MODE, GATE, KSTRUCT>(
+          st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][2][0][tid] : raw(0), A2[0],
+          bias);
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          if (FULL || j < static_cast<int>(valid)) {
-            FrontEnd fn = fe;
-            if (j + 1 < kChunk && (FULL || j + 1 < static_cast<int>(valid)))
-              fn = front_end<N, IO, MODE, GATE, STRUCT>(
-                  st.in[buf][0][j + 1][tid], st.in[buf][1][j + 1][tid],
-                  kZ ? st.in[buf][2][j + 1][tid] : raw(0), A2[0], bias);
-            float bc[2 * N];
-            read_bc<N>(st.bc[buf][j], bc, kC);
-            const raw y = update<N, IO, MODE, GATE, STRUCT>(fe, bc, A2, Dd, h, S, S_c);
-            if (MODE == kOutput) IO::bstore(y, ro, voff, (t0 + j) * row_bytes);
-            fe = fn;
-          }
+      for (int j = 0; j < kChunk; ++j) {
+        if (FULL || j < valid) {
+          // The step index passes through an empty asm statement, so this
+          // step's LDS addresses (and all work that depends on them) cannot be
+          // hoisted into earlier steps, where they would only hold registers.
+          int js = j;
+          asm volatile("" : "+s"(js));
+          FrontEnd fn = fe;
+          if (j + 1 < kChunk && (FULL || j + 1 < valid))
+            fn = front_end<N, IO, MODE, GATE, KSTRUCT>(
+                st.in[buf][0][js + 1][tid], st.in[buf][1][js + 1][tid],
+                kZ ? st.in[buf][2][js + 1][tid] : raw(0), A2[0], bias);
+          float bc[2 * N];
+          read_bc<N>(st.bc[buf][js], bc, kC);
+          const raw y = update<N, IO, MODE, GATE, KSTRUCT>(fe, bc, A2, Dd, h, S, S_c);
+          if (MODE == kOutput) st.yo[buf][js][tid] = y;
+          fe = fn;
+          // ... and this step's state update completes here, not after the
+          // later steps' loads (in the aggregate pass nothing else uses it)
+#pragma unroll
+          for (int n = 0; n < N; ++n) asm volatile("" : "+v"(h[n]));
         }
-      };
-      if (use_structured) {
-        if (more) body(std::true_type{}, std::true_type{});
-        else body(std::true_type{}, std::false_type{});
-      } else {
-        if (more) body(std::false_type{}, std::true_type{});
-        else body(std::false_type{}, std::false_type{});
       }
-      if (more) {
+      if (MORE) {
         land(buf ^ 1);
         if (tid < kTileElems) st.bc[buf ^ 1][bci / (2 * N)][bci % (2 * N)] = bcv;
         wait_vmem();
       }
       __syncthreads();
+    };
+    for (uint32_t c = 0; c + 1 < n_chunks; ++c) chunk(c, std::true_type{}, std::true_type{});
+    if (steps % kChunk == 0)
+      chunk(n_chunks - 1, std::false_type{}, std::true_type{});
+    else
+      chunk(n_chunks - 1, std::false_type{}, std::false_type{});
+    if (MODE == kOutput) {
+      const uint32_t last = n_chunks - 1;
+      store_tile<IO, CW>(ro, &st.yo[last & 1][0][0], row_bytes, last * kChunk, steps, valid_bytes,
+                         voff);
     }
   }
   if (!active) return;
@@ -442,20 +501,29 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
   if (plan.segments > 1) {
     const dim3 grid_agg(blocks, plan.segments - 1);
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW>), grid_agg, block, 0,
-                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, true>), grid_agg, block,
+                       0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s,
+                       g);
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, false>), grid_agg, block,
+                       0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s,
+                       g);
     const int64_t work = g.rows * N;
     const dim3 grid_c(static_cast<unsigned>((work + kBlock - 1) / kBlock));
     hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, block, 0, stream, p.A, ws_h, ws_s,
                        g.rows, p.dim, plan.segments);
   }
   const dim3 grid(blocks, plan.segments);
-  if (z)
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW>), grid, block, 0, stream, x,
-                       dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
-  else
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW>), grid, block, 0, stream, x,
-                       dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+  if (z) {
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, true>), grid, block, 0,
+                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, false>), grid, block, 0,
+                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+  } else {
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, true>), grid, block, 0,
+                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, false>), grid, block, 0,
+                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+  }
   return hipGetLastError();
 }
 
