@@ -86,19 +86,18 @@ struct Bf16Io {
   }
 };
 
-// softplus(u) = log(1 + e^u).
-// w = 1 + e^u is rounded; for w in [1, 2) the rounding error r = e^u - (w - 1)
-// is exact (w - 1 is exact there) and log(1 + e^u) = log(w) + r / w to first
-// order, with 1/w ~ 2 - w. For w >= 2 the rounding of w moves log(w) by less
-// than 2^-24 relative, so no correction is applied. Above u = 20 the result is
-// u to within e^-20 (and e^u may overflow), so u is returned.
+// softplus(u) = log(1 + e^u) = max(u, 0) + log(1 + e), e = e^-|u| in (0, 1].
+// w = 1 + e is rounded; as w lies in [1, 2], w - 1 is exact and
+// r = e - (w - 1) is the exact rounding error (1 + e = w + r). Then
+// log(1 + e) = log(w) + r / w to first order; adding r instead of r / w moves
+// the result by at most |r| (1 - 1/w) <= 2^-24 e, below 2^-23 of the result
+// (log(1 + e) >= e ln 2 on (0, 1]). e never overflows, so large u needs no
+// special case: the log term vanishes and max(u, 0) = u remains.
 __device__ __forceinline__ float softplus_f(float u) {
-  float e = hw_exp2(u * kLog2e);
-  float w = 1.0f + e;
-  float r = e - (w - 1.0f);
-  float inv_w = fmaxf(2.0f - w, 0.0f);
-  float s = fmaf(hw_log2(w), kLn2, r * inv_w);
-  return u > 20.0f ? u : s;
+  const float e = hw_exp2(-fabsf(u) * kLog2e);
+  const float w = 1.0f + e;
+  const float r = e - (w - 1.0f);
+  return fmaxf(u, 0.0f) + fmaf(hw_log2(w), kLn2, r);
 }
 
 // silu(v) = v * sigmoid(v) = v / (1 + e^-v). For v -> -inf, e^-v = inf and the

@@ -78,12 +78,10 @@ __device__ __forceinline__ FrontEnd front_end(typename IO::raw xr, typename IO::
 }
 
 // State update, read-out and epilogue of one step. Returns y in the io type.
-// The read-out sum runs as interleaved partial sums (a shorter dependency
-// chain than one serial accumulation).
+// The read-out accumulates into the D skip term, one multiply-add per state.
 template <int N, class IO, int MODE, bool GATE, bool STRUCTURED>
 __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const float (&bc)[2 * N],
-                                                   const float (&A2)[N], float Dd, float (&h)[N],
-                                                   float& S, float& S_c) {
+                                                   const float (&A2)[N], float Dd, float (&h)[N]) {
   float abar[N];
   if (STRUCTURED) {
     powers<N>(f.e, abar);
@@ -91,27 +89,16 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
 #pragma unroll
     for (int n = 0; n < N; ++n) abar[n] = hw_exp2(f.Delta * A2[n]);
   }
-  constexpr int P = N >= 4 ? 4 : N;
-  float acc[P];
-#pragma unroll
-  for (int k = 0; k < P; ++k) acc[k] = 0.0f;
+  float y = Dd * f.xf;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     h[n] = fmaf(abar[n], h[n], f.dx * bc[n]);
-    if (MODE == kOutput) acc[n % P] = fmaf(bc[N + n], h[n], acc[n % P]);
+    if (MODE == kOutput) y = fmaf(bc[N + n], h[n], y);
   }
   if (MODE == kOutput) {
-    float y = acc[0];
-#pragma unroll
-    for (int k = 1; k < P; ++k) y += acc[k];
-    y = fmaf(Dd, f.xf, y);
     if (GATE) y *= f.gate;
     return IO::from_f32(y);
   }
-  const float v = f.Delta - S_c;
-  const float tsum = S + v;
-  S_c = (tsum - S) - v;
-  S = tsum;
   return typename IO::raw(0);
 }
 
@@ -267,13 +254,32 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // CW: bytes per lane of each global-to-LDS copy: 16 when every channel tile
 // is a whole number of 16-byte pieces, 4 when of 32-bit words, and 0 for the
 // register-staged copy otherwise.
-// Occupancy target: five 256-lane workgroups per CU (five waves per SIMD), so
-// the compiler keeps each lane within 102 vector registers instead of hoisting
-// loads of later steps.
-constexpr int kMinBlocksPerCU = 5;
+// Decay paths compiled into one kernel: kPathGeneral (exp per state),
+// kPathStructured (powers of one exponential, for S4D-Real-shaped A), or both
+// behind a per-workgroup branch.
+enum PathSet { kPathGeneral = 0, kPathStructured = 1, kPathBoth = 2 };
 
-template <int N, class IO, int MODE, bool GATE, int CW, bool KSTRUCT>
-__global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
+#ifndef MSCAN_FUSED_PATHS
+#define MSCAN_FUSED_PATHS 0
+#endif
+#ifndef MSCAN_OUT_WAVES
+#define MSCAN_OUT_WAVES 4
+#endif
+#ifndef MSCAN_AGG_WAVES
+#define MSCAN_AGG_WAVES 5
+#endif
+
+// Occupancy targets, in 256-lane workgroups per CU (= waves per SIMD): the
+// output pass stages x, Delta_raw, z and y (35 KB of LDS per workgroup), so at
+// most four fit in a CU's 160 KB; the aggregate pass stages x and Delta_raw
+// only and runs five. The bound keeps the compiler within the matching
+// register budget (128 or 102 vector registers per lane) instead of hoisting
+// loads of later steps.
+template <int MODE>
+constexpr int kMinBlocksPerCU = MODE == kOutput ? MSCAN_OUT_WAVES : MSCAN_AGG_WAVES;
+
+template <int N, class IO, int MODE, bool GATE, int CW, int PATHS>
+__global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_kernel(
     const typename IO::raw* __restrict__ x, const typename IO::raw* __restrict__ delta,
     const float* __restrict__ A, const typename IO::raw* __restrict__ B,
     const typename IO::raw* __restrict__ C, const float* __restrict__ D,
@@ -301,8 +307,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
   const uint32_t steps = static_cast<uint32_t>(t_end - t_begin);
   const int64_t row = b * g.dim + d;
 
-  // S4D-Real-shaped rows (A[d, n] = (n + 1) A[d, 0]) get their N decays as
-  // powers of one exponential; the path is chosen per workgroup.
   float A2[N];
   bool structured = true;
   const float a0 = A[d * N];
@@ -339,9 +343,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
   const raw* Cp = C + (b * g.seqlen + t_begin) * N;
   const int bci = tid % kTileElems;  // this thread's B/C tile element
 
-  // Each launch covers either the S4D-Real-shaped tiles or the others; a
-  // workgroup of the other kind leaves at once (the whole group together).
-  if (__syncthreads_and(structured) != KSTRUCT) return;
   float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta (aggregate mode)
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
   // in registers on the register-staged path until land() writes them)
@@ -364,7 +365,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
       if (kZ) store_tile_regs<IO>(rgz, &st.in[nb][2][0][0]);
     }
   };
-  if (steps > 0) {
+  // The whole segment, for S4D-Real-shaped tiles (powers of one decay) or
+  // for general A; the branch is uniform over the workgroup.
+  auto run = [&](auto struct_tag) {
+    constexpr bool KSTRUCT = decltype(struct_tag)::value;
     // chunk 0 into buffer 0
     fetch(0, 0);
     float bcv = bc_elem<N, IO>(Bp, Cp, 0, steps, bci);
@@ -392,6 +396,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
       FrontEnd fe = front_end<N, IO, MODE, GATE, KSTRUCT>(
           st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][2][0][tid] : raw(0), A2[0],
           bias);
+      float dsum = 0.0f;  // this chunk's Delta (aggregate mode)
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         if (FULL || j < valid) {
@@ -407,14 +412,21 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
                 kZ ? st.in[buf][2][js + 1][tid] : raw(0), A2[0], bias);
           float bc[2 * N];
           read_bc<N>(st.bc[buf][js], bc, kC);
-          const raw y = update<N, IO, MODE, GATE, KSTRUCT>(fe, bc, A2, Dd, h, S, S_c);
+          const raw y = update<N, IO, MODE, GATE, KSTRUCT>(fe, bc, A2, Dd, h);
           if (MODE == kOutput) st.yo[buf][js][tid] = y;
+          if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
           // ... and this step's state update completes here, not after the
           // later steps' loads (in the aggregate pass nothing else uses it)
 #pragma unroll
           for (int n = 0; n < N; ++n) asm volatile("" : "+v"(h[n]));
         }
+      }
+      if (MODE == kAggregate) {
+        const float v = dsum - S_c;
+        const float tsum = S + v;
+        S_c = (tsum - S) - v;
+        S = tsum;
       }
       if (MORE) {
         land(buf ^ 1);
@@ -432,6 +444,20 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU) void scan_segment_kernel(
       const uint32_t last = n_chunks - 1;
       store_tile<IO, CW>(ro, &st.yo[last & 1][0][0], row_bytes, last * kChunk, steps, valid_bytes,
                          voff);
+    }
+  };
+  // S4D-Real-shaped rows (A[d, n] = (n + 1) A[d, 0]) get their N decays as
+  // powers of one exponential when the whole tile is of that shape. A
+  // workgroup whose path this kernel does not hold leaves at once (the whole
+  // group together): the launch for the other path writes its results.
+  const bool tile_structured = __syncthreads_and(structured);
+  if (PATHS == kPathStructured && !tile_structured) return;
+  if (PATHS == kPathGeneral && tile_structured) return;
+  if (steps > 0) {
+    if (tile_structured) {
+      if constexpr (PATHS != kPathGeneral) run(std::true_type{});
+    } else {
+      if constexpr (PATHS != kPathStructured) run(std::false_type{});
     }
   }
   if (!active) return;
@@ -499,14 +525,18 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
 
   const dim3 block(kBlock);
   const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
+  // one launch per decay path, or one for both
+  constexpr int kFirst = MSCAN_FUSED_PATHS ? kPathBoth : kPathStructured;
+  constexpr bool kSecond = !MSCAN_FUSED_PATHS;
   if (plan.segments > 1) {
     const dim3 grid_agg(blocks, plan.segments - 1);
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, true>), grid_agg, block,
-                       0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s,
-                       g);
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, false>), grid_agg, block,
-                       0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s,
-                       g);
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, kFirst>), grid_agg,
+                       block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h,
+                       ws_s, g);
+    if (kSecond)
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, kPathGeneral>),
+                         grid_agg, block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out,
+                         p.last_state, ws_h, ws_s, g);
     const int64_t work = g.rows * N;
     const dim3 grid_c(static_cast<unsigned>((work + kBlock - 1) / kBlock));
     hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, block, 0, stream, p.A, ws_h, ws_s,
@@ -514,15 +544,19 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   }
   const dim3 grid(blocks, plan.segments);
   if (z) {
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, true>), grid, block, 0,
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, kFirst>), grid, block, 0,
                        stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, false>), grid, block, 0,
-                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+    if (kSecond)
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, kPathGeneral>), grid,
+                         block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state,
+                         ws_h, ws_s, g);
   } else {
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, true>), grid, block, 0,
+    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, kFirst>), grid, block, 0,
                        stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
-    hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, false>), grid, block, 0,
-                       stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state, ws_h, ws_s, g);
+    if (kSecond)
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, kPathGeneral>), grid,
+                         block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state,
+                         ws_h, ws_s, g);
   }
   return hipGetLastError();
 }
