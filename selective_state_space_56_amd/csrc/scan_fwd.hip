@@ -400,11 +400,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         if (FULL || j < valid) {
-          // The step index passes through an empty asm statement, so this
-          // step's LDS addresses (and all work that depends on them) cannot be
-          // hoisted into earlier steps, where they would only hold registers.
-          int js = j;
-          asm volatile("" : "+s"(js));
+          const int js = j;
           FrontEnd fn = fe;
           if (j + 1 < kChunk && (FULL || j + 1 < valid))
             fn = front_end<N, IO, MODE, GATE, KSTRUCT>(
@@ -416,8 +412,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           if (MODE == kOutput) st.yo[buf][js][tid] = y;
           if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
-          // ... and this step's state update completes here, not after the
-          // later steps' loads (in the aggregate pass nothing else uses it)
+          // This step's state update completes here, not after later steps'
+          // loads (in the aggregate pass nothing else uses it, and hoisted
+          // loads would only hold registers).
 #pragma unroll
           for (int n = 0; n < N; ++n) asm volatile("" : "+v"(h[n]));
         }
