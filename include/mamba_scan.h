@@ -84,8 +84,11 @@ typedef struct mamba_scan_desc {
 
 /*
  * Bytes of device workspace mamba_scan_fwd needs for this problem (0 when
- * none). The amount depends only on the sizes in `desc`. Returns 0 for an
- * invalid descriptor as well; mamba_scan_fwd reports the error.
+ * none). The amount depends on the sizes in `desc` and, unless bits 0-15 of
+ * flags fix the number of time segments, on the compute-unit count of the
+ * current HIP device (call it with the device current that the scan will run
+ * on). Returns 0 for an invalid descriptor as well; mamba_scan_fwd reports
+ * the error.
  */
 size_t mamba_scan_workspace_size(const mamba_scan_desc *desc);
 

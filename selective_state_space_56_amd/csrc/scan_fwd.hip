@@ -19,6 +19,7 @@
 //      aggregates into each segment's carry-in state;
 //   3. output: every segment re-scans from its carry-in and writes y (and the
 //      last one the final state).
+#include <atomic>
 #include <type_traits>
 
 #include "device_math.h"
@@ -38,6 +39,7 @@ struct Dims {
   int64_t seg_len;
   int segments;
   unsigned tiles;   // channel tiles of kBlock per batch row
+  uint32_t* tile_flags;  // per channel tile: 1 = S4D-Real shaped (workspace), or null
 };
 
 enum Mode { kOutput = 0, kAggregate = 1 };
@@ -339,15 +341,32 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const uint32_t steps = static_cast<uint32_t>(t_end - t_begin);
   const int64_t row = b * g.dim + d;
 
-  float A2[N];
-  bool structured = true;
-  const float a0 = A[d * N];
+  // Decay path of the workgroup's channel tile: S4D-Real shaped when
+  // A[d, n] = (n + 1) A[d, 0] for every channel of the tile (its N decays are
+  // then powers of one exponential), general otherwise. With a workspace, the
+  // first aggregate launch classifies each tile and records it in tile_flags
+  // (the copy in batch row 0, segment 0 writes); later launches read the flag.
+  // A workgroup whose path this kernel does not hold leaves at once (the whole
+  // group together): the launch for the other path writes its results.
+  const unsigned tile = blockIdx.x % g.tiles;
+  bool tile_structured;
+  if (g.tile_flags == nullptr || (MODE == kAggregate && PATHS != kPathGeneral)) {
+    bool structured = true;
+    const float a0 = A[d * N];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const float an = A[d * N + n];
-    structured = structured && (an == static_cast<float>(n + 1) * a0);
-    A2[n] = an * kLog2e;
+    for (int n = 1; n < N; ++n) structured = structured && (A[d * N + n] == (n + 1) * a0);
+    tile_structured = __syncthreads_and(structured);
+    if (g.tile_flags != nullptr && b == 0 && s == 0 && tid == 0)
+      g.tile_flags[tile] = tile_structured ? 1u : 0u;
+  } else {
+    tile_structured = g.tile_flags[tile] != 0u;
   }
+  if (PATHS == kPathStructured && !tile_structured) return;
+  if (PATHS == kPathGeneral && tile_structured) return;
+
+  float A2[N];  // A[d, n] log2(e) (the structured path uses A2[0] only)
+#pragma unroll
+  for (int n = 0; n < N; ++n) A2[n] = A[d * N + n] * kLog2e;
   const float Dd = (MODE == kOutput && D) ? D[d] : 0.0f;
   const float bias = bias_p ? bias_p[d] : 0.0f;
 
@@ -480,13 +499,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       for (int n = 0; n < N; ++n) h[n] *= dx_prev;  // back from g to h
     }
   };
-  // S4D-Real-shaped rows (A[d, n] = (n + 1) A[d, 0]) get their N decays as
-  // powers of one exponential when the whole tile is of that shape. A
-  // workgroup whose path this kernel does not hold leaves at once (the whole
-  // group together): the launch for the other path writes its results.
-  const bool tile_structured = __syncthreads_and(structured);
-  if (PATHS == kPathStructured && !tile_structured) return;
-  if (PATHS == kPathGeneral && tile_structured) return;
   if (steps > 0) {
     if (tile_structured) {
       if constexpr (PATHS != kPathGeneral) run(std::true_type{});
@@ -512,23 +524,40 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
 
 // Fold the segment aggregates of one (row, n) in time order. Slot k of the
 // workspace holds segment k's (end state from zero, sum of Delta) on entry and
-// the carry-in state of segment k + 1 on exit.
+// the carry-in state of segment k + 1 on exit. The slots are read in blocks of
+// kFoldBlock before they are folded and written, so the loads of a block are
+// in flight together.
+constexpr int kFoldBlock = 8;
+
 template <int N>
-__global__ __launch_bounds__(kBlock) void scan_combine_kernel(const float* A, float* ws_h,
-                                                              const float* ws_s, int64_t rows,
-                                                              int64_t dim, int segments) {
+__global__ __launch_bounds__(kBlock) void scan_combine_kernel(const float* __restrict__ A,
+                                                              float* __restrict__ ws_h,
+                                                              const float* __restrict__ ws_s,
+                                                              int64_t rows, int64_t dim,
+                                                              int segments) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
   if (i >= rows * N) return;
   const int64_t row = i / N;
   const int n = static_cast<int>(i % N);
   const int64_t d = row % dim;
   const float a2 = A[d * N + n] * kLog2e;
+  const int aggs = segments - 1;
   float h = 0.0f;
-  for (int k = 0; k < segments - 1; ++k) {
-    float* slot = ws_h + static_cast<int64_t>(k) * rows * N + i;
-    const float decay = hw_exp2(a2 * ws_s[static_cast<int64_t>(k) * rows + row]);
-    h = fmaf(decay, h, *slot);
-    *slot = h;
+  for (int k0 = 0; k0 < aggs; k0 += kFoldBlock) {
+    float hv[kFoldBlock], sv[kFoldBlock];
+#pragma unroll
+    for (int u = 0; u < kFoldBlock; ++u) {
+      const int k = k0 + u < aggs ? k0 + u : aggs - 1;
+      hv[u] = ws_h[static_cast<int64_t>(k) * rows * N + i];
+      sv[u] = ws_s[static_cast<int64_t>(k) * rows + row];
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBlock; ++u) {
+      if (k0 + u < aggs) {
+        h = fmaf(hw_exp2(a2 * sv[u]), h, hv[u]);
+        ws_h[static_cast<int64_t>(k0 + u) * rows * N + i] = h;
+      }
+    }
   }
 }
 
@@ -550,6 +579,9 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.tiles = static_cast<unsigned>((p.dim + kBlock - 1) / kBlock);
   float* ws_h = static_cast<float*>(workspace);
   float* ws_s = ws_h ? ws_h + static_cast<int64_t>(plan.segments - 1) * g.rows * N : nullptr;
+  g.tile_flags = ws_s ? reinterpret_cast<uint32_t*>(ws_s + static_cast<int64_t>(plan.segments - 1) *
+                                                               g.rows)
+                      : nullptr;
   const raw* x = static_cast<const raw*>(p.x);
   const raw* dl = static_cast<const raw*>(p.delta);
   const raw* B = static_cast<const raw*>(p.B);
@@ -625,6 +657,22 @@ hipError_t dispatch_n(const ScanProblem& p, const ScanPlan& plan, void* ws, hipS
 
 }  // namespace
 
+// Compute units of the current device, queried once per device (256, the
+// full gfx950 part, when no device can be queried).
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments) {
   ScanPlan plan{seqlen, 1, 0};
   const int64_t rows = batch * dim;
@@ -633,12 +681,15 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
   if (forced_segments > 0) {
     segs = forced_segments;
   } else {
-    // A wave issues at most one vector instruction every few cycles, so each
-    // SIMD (256 CUs x 4) needs several waves: aim for about six per SIMD when
-    // the rows alone cannot provide them, with segments of 32 steps or more.
-    const int64_t target_lanes = 256LL * 4 * 64 * 6;
-    segs = (target_lanes + rows - 1) / rows;
-    const int64_t max_by_len = seqlen / 32 > 0 ? seqlen / 32 : 1;
+    // Both passes are bound by vector-ALU issue, which a SIMD sustains from
+    // about two resident waves on. Cut the sequence into as many segments as
+    // keep the output launch within two rounds of resident workgroups (the
+    // aggregate pass redoes (segments - 1) / segments of the work, so more
+    // segments cost more), each segment at least 48 steps long.
+    const int64_t blocks = batch * ((dim + kBlock - 1) / kBlock);
+    const int64_t slots = static_cast<int64_t>(device_cus()) * kMinBlocksPerCU<kOutput>;
+    segs = 2 * slots / blocks;
+    const int64_t max_by_len = seqlen / 48;
     if (segs > max_by_len) segs = max_by_len;
   }
   if (segs > 4096) segs = 4096;
@@ -653,9 +704,12 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
   plan.seg_len = seg_len;
   plan.segments = static_cast<int>(segs);
   if (segs > 1) {
+    // segment aggregates (end states and Delta sums), then one flag per
+    // channel tile
     const size_t floats = static_cast<size_t>(segs - 1) * static_cast<size_t>(rows) *
                           static_cast<size_t>(dstate + 1);
-    plan.workspace_bytes = (floats * sizeof(float) + 255) / 256 * 256;
+    const size_t tiles = static_cast<size_t>((dim + kBlock - 1) / kBlock);
+    plan.workspace_bytes = (floats * sizeof(float) + tiles * sizeof(uint32_t) + 255) / 256 * 256;
   }
   return plan;
 }
