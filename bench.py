@@ -27,7 +27,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
-ALU_PEAK_TFLOPS = 157.3    # MI355X fp32 vector (256 CUs at 2.4 GHz)
+# fp32 vector peak without packed (two-per-lane) arithmetic, which these
+# kernels do not use: 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2.4 GHz.
+# The published 157.3 TFLOP/s counts packed fp32 FMAs.
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+PUBLISHED_FP32_VECTOR_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "scan": ["scan_fwd.hip", "device_math.h", "kernels.h"],
+    "decode": ["state_update.hip", "device_math.h", "kernels.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    """sha256 over the kernel sources of one entry point (to tell whether HBM
+    byte counts recorded under profiles/ still describe the built kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "selective_state_space_56_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kind: str, workload: str):
+    """HBM bytes per call measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a plain copy's counts) and stored in profiles/, or None when
+    there is no record or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kind}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_call")
 METRIC = "scan fwd: (batch·L·D_inner) elem-steps/s + achieved HBM GB/s (% of peak)"
 
 
@@ -96,7 +130,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mamba2p8b_prefill")
     ap.add_argument("--segments", type=int, default=0, help="force time segments (0 = library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -175,13 +209,15 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "d_inner": w.dim,
                    "d_state": w.dstate, "io": w.io, "state": "f32", "gate": w.gate,
                    "parallelism": "single GPU"},
-        # The scan is bound by vector-ALU issue (see the design notes), so the
-        # roofline is the ALU one; the HBM view (the metric's GB/s) rides along.
+        # The scan is bound by vector-ALU issue, so the roofline is the ALU
+        # one; the HBM view (the metric's GB/s) rides along.
         "roofline": {"bound": "alu", "achieved": tflops, "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / ALU_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / ALU_PEAK_TFLOPS,
+                     "traffic": recorded_traffic("scan", w.name),
                      "kernel": "mamba_scan_fwd call (aggregate, fold and output kernels)",
                      "algorithmic_flops_per_launch": nflops, "avg_launch_ms": kern_ms,
-                     "min_launch_ms": min(per_call), "workspace_bytes": ws_bytes},
+                     "min_launch_ms": min(per_call), "workspace_bytes": ws_bytes,
+                     "published_fp32_vector_peak": PUBLISHED_FP32_VECTOR_TFLOPS},
         "hbm": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes},
     }
@@ -214,7 +250,8 @@ def main():
             "avg_launch_ms": dms,
             "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_launch": db},
+                         "traffic": recorded_traffic("decode", wd.name),
+                         "algorithmic_bytes_per_launch": db},
         }
         del toks, state
 
