@@ -36,6 +36,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            0x7fffffff, 0x00020000);
 }
+// The same over `bytes` bytes from `base` (at most 0x7fffffff): offsets at or
+// past the end read 0 and drop stores. With a wave-uniform base and size it is
+// built in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
 
 // Storage types for the io tensors.
 //   load_pair(p, k): elements 2k and 2k + 1 of a wave-uniform constant array,
@@ -57,6 +64,10 @@ struct F32Io {
   }
   static __device__ __forceinline__ float to_f32(raw v) { return v; }
   static __device__ __forceinline__ raw from_f32(float v) { return v; }
+  // bitwise or of two raw values (one of them 0)
+  static __device__ __forceinline__ raw bit_or(raw a, raw b) {
+    return __uint_as_float(__float_as_uint(a) | __float_as_uint(b));
+  }
 };
 
 struct Bf16Io {
@@ -71,6 +82,8 @@ struct Bf16Io {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
   }
   static __device__ __forceinline__ float load(const raw* p) { return to_f32(*p); }
+  // bitwise or of two raw values (one of them 0)
+  static __device__ __forceinline__ raw bit_or(raw a, raw b) { return static_cast<raw>(a | b); }
   static __device__ __forceinline__ raw bload(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);

@@ -136,13 +136,13 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
   return typename IO::raw(0);
 }
 
-// Scan `steps` steps of the workgroup's rows. The buffer resources start at
-// the (batch, first step, first channel of the tile) element of each tensor;
-// the lane's channel is the per-lane byte offset `voff` (kOffNone for lanes
-// past the last channel: they read zeros and their stores are dropped) and
-// the step is the wave-uniform offset step * row_bytes. Steps run in chunks of
-// kChunk: the next chunk's inputs are requested before the current chunk is
-// computed, and each step's state-free front-end one step ahead.
+// Steps run in chunks of kChunk: the next chunk's inputs are requested before
+// the current chunk is computed, and each step's state-free front-end one step
+// ahead. Global accesses of a chunk go through buffer resources that start at
+// the chunk's first step and end at the segment's end (built in scalar
+// registers per chunk), with per-lane offsets fixed for the whole segment:
+// rows past the segment read as zero and are never used; channels past the
+// last one read as zero and their stores are dropped.
 // LDS staging of one chunk of kChunk steps for the workgroup's channel tile:
 // x, Delta_raw and z as stored (raw io values) and B_t, C_t widened to fp32.
 // Two buffers: the next chunk is fetched while the current one is computed.
@@ -157,66 +157,83 @@ struct __align__(16) Stage {
 
 using lds_void = __attribute__((address_space(3))) void;
 
-// Copy rows t0 .. t0 + kChunk - 1 of one input tensor's channel tile straight
-// from global memory into LDS (buffer_load ... lds: no registers involved).
-// Each lane moves S bytes; lane i of a wave lands S * i bytes after the
-// wave's LDS base. Rows past the segment and bytes past the last channel are
-// out of range (the hardware reads them as zero); they are never used.
+// Per-lane byte offset of a tile piece: a tile of kChunk rows (steps) by
+// kBlock channels is moved S bytes per lane, lane i of instruction k taking
+// the piece (k * kBlock + i) * S bytes into the tile; each instruction covers
+// S / eb whole rows, so the offset within the instruction's rows is the same
+// for every k. Pieces past the last channel get kOffNone.
 template <class IO, int S>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, typename IO::raw* tile,
-                                         uint32_t row_bytes, uint32_t t0, uint32_t steps,
-                                         uint32_t valid_bytes) {
+__device__ __forceinline__ uint32_t tile_lane_offset(uint32_t row_bytes, uint32_t valid_bytes) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const uint32_t flat = threadIdx.x * S;
+  const uint32_t row = flat / (kBlock * eb), col = flat % (kBlock * eb);
+  return col + S <= valid_bytes ? row * row_bytes + col : kOffNone;
+}
+
+// Copy rows 0 .. kChunk - 1 (from `rows`, the tile's first element in the
+// chunk's first step) of one input tensor's channel tile straight from global
+// memory into LDS (buffer_load ... lds: no registers involved). Each copy
+// instruction gets its own buffer resource, built in scalar registers, that
+// starts at its first row and ends at the segment's end (`rows_left` rows from
+// `rows`): rows past the segment read as zero, as do pieces past the last
+// channel (`lane_off`); they are never used. Lane i of wave `wv` lands S * i
+// bytes after the wave's LDS base.
+template <class IO, int S>
+__device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t rows_left,
+                                         uint32_t row_bytes, typename IO::raw* tile, int wv,
+                                         uint32_t lane_off) {
   constexpr int eb = sizeof(typename IO::raw);
   constexpr int kTileBytes = kChunk * kBlock * eb;
   constexpr int kPerInstr = kBlock * S;
+  constexpr int kRowsPerInstr = S / eb;
   static_assert(kTileBytes % kPerInstr == 0, "tile must be a whole number of copies");
-  const int w = threadIdx.x / 64, i = threadIdx.x % 64;
+  static_assert(S == 16 || S == 4, "copies are 16 or 4 bytes per lane");
 #pragma unroll
   for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
-    const int flat = (k * kBlock + w * 64 + i) * S;
-    const int row = flat / (kBlock * eb), col = flat % (kBlock * eb);
-    const uint32_t t = t0 + row;
-    const uint32_t voff =
-        (t < steps && static_cast<uint32_t>(col + S) <= valid_bytes) ? t * row_bytes + col : kOffNone;
-    char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + w * 64) * S;
-    static_assert(S == 16 || S == 4, "copies are 16 or 4 bytes per lane");
+    const uint32_t r0 = k * kRowsPerInstr;
+    const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+    const auto r = make_rsrc(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
+    char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + wv * 64) * S;
     if constexpr (S == 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, lane_off, 0, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, lane_off, 0, 0, 0);
   }
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Write the y tile of the chunk at step t0 from LDS to HBM: S bytes per lane
-// (the same pieces as dma_tile), or, with S == 0, each lane its own channel.
+// Write the y tile of one chunk from LDS to HBM in the pieces of dma_tile
+// (same per-instruction resources, so rows past the segment are dropped), or,
+// with S == 0, each lane its own channel (`ch_off`, kOffNone past the last
+// channel) row by row.
 template <class IO, int S>
-__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t r, const typename IO::raw* tile,
-                                           uint32_t row_bytes, uint32_t t0, uint32_t steps,
-                                           uint32_t valid_bytes, uint32_t voff) {
+__device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows_left,
+                                           uint32_t row_bytes, const typename IO::raw* tile,
+                                           uint32_t lane_off, uint32_t ch_off) {
   constexpr int eb = sizeof(typename IO::raw);
   const int tid = threadIdx.x;
   if constexpr (S == 0) {
+    const auto r = make_rsrc(rows);
 #pragma unroll
     for (int j = 0; j < kChunk; ++j)
-      if (t0 + j < steps) IO::bstore(tile[j * kBlock + tid], r, voff, (t0 + j) * row_bytes);
+      if (static_cast<uint32_t>(j) < rows_left)
+        IO::bstore(tile[j * kBlock + tid], r, ch_off, j * row_bytes);
   } else {
     constexpr int kTileBytes = kChunk * kBlock * eb;
     constexpr int kPerInstr = kBlock * S;
+    constexpr int kRowsPerInstr = S / eb;
 #pragma unroll
     for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
-      const int flat = (k * kBlock + tid) * S;
-      const int row = flat / (kBlock * eb), col = flat % (kBlock * eb);
-      const uint32_t t = t0 + row;
-      const uint32_t o = (t < steps && static_cast<uint32_t>(col + S) <= valid_bytes)
-                             ? t * row_bytes + col
-                             : kOffNone;
-      const char* src = reinterpret_cast<const char*>(tile) + flat;
+      const uint32_t r0 = k * kRowsPerInstr;
+      const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+      const auto r = make_rsrc(reinterpret_cast<char*>(rows) + r0 * row_bytes, left * row_bytes);
+      const char* src = reinterpret_cast<const char*>(tile) + (k * kBlock + tid) * S;
       if constexpr (S == 16)
-        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, lane_off, 0, 0);
       else
-        __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), r, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), r, lane_off, 0,
+                                              0);
     }
   }
 }
@@ -231,12 +248,13 @@ struct TileRegs {
 };
 
 template <class IO>
-__device__ __forceinline__ void load_tile_regs(TileRegs<IO>& tr, __amdgpu_buffer_rsrc_t r,
-                                               uint32_t voff, uint32_t row_bytes, uint32_t t0,
-                                               uint32_t steps) {
+__device__ __forceinline__ void load_tile_regs(TileRegs<IO>& tr, const typename IO::raw* rows,
+                                               uint32_t rows_left, uint32_t row_bytes,
+                                               uint32_t ch_off) {
+  const auto r = make_rsrc(rows);
 #pragma unroll
   for (int j = 0; j < kChunk; ++j)
-    tr.v[j] = IO::bload(r, t0 + j < steps ? voff : kOffNone, (t0 + j) * row_bytes);
+    tr.v[j] = IO::bload(r, static_cast<uint32_t>(j) < rows_left ? ch_off : kOffNone, j * row_bytes);
 }
 
 template <class IO>
@@ -245,18 +263,31 @@ __device__ __forceinline__ void store_tile_regs(const TileRegs<IO>& tr, typename
   for (int j = 0; j < kChunk; ++j) tile[j * kBlock + threadIdx.x] = tr.v[j];
 }
 
-// Element `i` of the B/C tile of the chunk at step c0 (i < kChunk * 2N; B or C
-// of step i / 2N, state i % 2N, C when i % 2N >= N). Steps at or past
-// `steps` are clamped to the last step (their values are never used).
+// Thread i < kChunk * 2N fetches element i of a chunk's B/C tile: B or C of
+// step i / 2N, state i % 2N (C when i % 2N >= N). Its byte offsets into B and
+// into C (kOffNone for the tensor it does not read, and for i past the tile):
+struct BcOffsets {
+  uint32_t b, c;
+};
 template <int N, class IO>
-__device__ __forceinline__ float bc_elem(const typename IO::raw* __restrict__ Bp,
-                                         const typename IO::raw* __restrict__ Cp, uint32_t c0,
-                                         uint32_t steps, int i) {
+__device__ __forceinline__ BcOffsets bc_offsets(int i) {
+  constexpr int eb = sizeof(typename IO::raw);
   const int j = i / (2 * N), k = i % (2 * N);
-  uint32_t t = c0 + j;
-  t = t < steps ? t : steps - 1;
-  return k < N ? IO::load(Bp + static_cast<size_t>(t) * N + k)
-               : IO::load(Cp + static_cast<size_t>(t) * N + (k - N));
+  const bool in_tile = i < kChunk * 2 * N;
+  return {in_tile && k < N ? static_cast<uint32_t>((j * N + k) * eb) : kOffNone,
+          in_tile && k >= N ? static_cast<uint32_t>((j * N + k - N) * eb) : kOffNone};
+}
+
+// This thread's B/C tile element for the chunk whose first step is row 0 of
+// Bc / Cc (`rows_left` steps to the segment's end; steps past it read 0 and are
+// never used), widened to fp32.
+template <int N, class IO>
+__device__ __forceinline__ float bc_elem(const typename IO::raw* Bc, const typename IO::raw* Cc,
+                                         uint32_t rows_left, BcOffsets o) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const uint32_t bytes = rows_left * N * eb;
+  const auto rb = make_rsrc(Bc, bytes), rc = make_rsrc(Cc, bytes);
+  return IO::to_f32(IO::bit_or(IO::bload(rb, o.b, 0), IO::bload(rc, o.c, 0)));
 }
 
 template <int N>
@@ -385,29 +416,47 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const uint32_t row_bytes = static_cast<uint32_t>(g.dim * eb);
   const int64_t left = g.dim - d0;
   const uint32_t valid_bytes = static_cast<uint32_t>((left < kBlock ? left : kBlock) * eb);
-  const uint32_t voff = active ? tid * eb : kOffNone;
-  const auto rx = make_rsrc(x + row0);
-  const auto rd = make_rsrc(delta + row0);
-  const auto rz = make_rsrc(kZ ? z + row0 : x + row0);
-  const auto ro = make_rsrc(out + row0);
+  const uint32_t ch_off = active ? tid * eb : kOffNone;  // this lane's channel in a row
+  // per-lane offset of the tile pieces this lane copies (CW > 0)
+  const uint32_t lane_off = CW != 0 ? tile_lane_offset<IO, (CW != 0 ? CW : 4)>(row_bytes, valid_bytes)
+                                    : 0u;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, wave-uniform
+  // first element of the tile in the segment's first step, per tensor
+  const raw* x0 = x + row0;
+  const raw* dl0 = delta + row0;
+  const raw* z0 = kZ ? z + row0 : x + row0;
+  raw* out0 = out + row0;
   const raw* Bp = B + (b * g.seqlen + t_begin) * N;
   const raw* Cp = C + (b * g.seqlen + t_begin) * N;
-  const int bci = tid % kTileElems;  // this thread's B/C tile element
+  const BcOffsets bco = bc_offsets<N, IO>(tid);  // this thread's B/C tile element
+  const int bci = tid % kTileElems;
 
   float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta (aggregate mode)
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
   // in registers on the register-staged path until land() writes them)
   TileRegs<IO> rgx, rgd, rgz;
   auto fetch = [&](int nb, uint32_t t1) {
+    const int64_t at = static_cast<int64_t>(t1) * g.dim;
+    const uint32_t left = steps - t1;
     if constexpr (CW != 0) {
-      dma_tile<IO, CW>(rx, &st.in[nb][0][0][0], row_bytes, t1, steps, valid_bytes);
-      dma_tile<IO, CW>(rd, &st.in[nb][1][0][0], row_bytes, t1, steps, valid_bytes);
-      if (kZ) dma_tile<IO, CW>(rz, &st.in[nb][2][0][0], row_bytes, t1, steps, valid_bytes);
+      dma_tile<IO, CW>(x0 + at, left, row_bytes, &st.in[nb][0][0][0], wv, lane_off);
+      dma_tile<IO, CW>(dl0 + at, left, row_bytes, &st.in[nb][1][0][0], wv, lane_off);
+      if (kZ) dma_tile<IO, CW>(z0 + at, left, row_bytes, &st.in[nb][2][0][0], wv, lane_off);
     } else {
-      load_tile_regs<IO>(rgx, rx, voff, row_bytes, t1, steps);
-      load_tile_regs<IO>(rgd, rd, voff, row_bytes, t1, steps);
-      if (kZ) load_tile_regs<IO>(rgz, rz, voff, row_bytes, t1, steps);
+      load_tile_regs<IO>(rgx, x0 + at, left, row_bytes, ch_off);
+      load_tile_regs<IO>(rgd, dl0 + at, left, row_bytes, ch_off);
+      if (kZ) load_tile_regs<IO>(rgz, z0 + at, left, row_bytes, ch_off);
     }
+  };
+  // this thread's B/C element of the chunk at step t1
+  auto fetch_bc = [&](uint32_t t1) {
+    return bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
+                          steps - t1, bco);
+  };
+  // y tile of the chunk at step t1 from LDS buffer yb to HBM
+  auto put_y = [&](int yb, uint32_t t1) {
+    store_tile<IO, CW>(out0 + static_cast<int64_t>(t1) * g.dim, steps - t1, row_bytes,
+                       &st.yo[yb][0][0], lane_off, ch_off);
   };
   auto land = [&](int nb) {
     if constexpr (CW == 0) {
@@ -423,7 +472,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     float dx_prev = 1.0f;  // structured rows: h holds g = h / dx_prev
     // chunk 0 into buffer 0
     fetch(0, 0);
-    float bcv = bc_elem<N, IO>(Bp, Cp, 0, steps, bci);
+    float bcv = fetch_bc(0);
     land(0);
     if (tid < kTileElems) st.bc[0][bci / (2 * N)][bci % (2 * N)] = bcv;
     wait_vmem();
@@ -438,11 +487,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       const int buf = c & 1;
       const uint32_t t0 = c * kChunk;
       if (MODE == kOutput && c > 0)
-        store_tile<IO, CW>(ro, &st.yo[buf ^ 1][0][0], row_bytes, t0 - kChunk, steps, valid_bytes,
-                           voff);
+        put_y(buf ^ 1, t0 - kChunk);
       if (MORE) {
         fetch(buf ^ 1, t0 + kChunk);
-        bcv = bc_elem<N, IO>(Bp, Cp, t0 + kChunk, steps, bci);
+        bcv = fetch_bc(t0 + kChunk);
       }
       const int valid = FULL ? kChunk : static_cast<int>(steps - t0);
       FrontEnd fe = front_end<N, IO, MODE, GATE, KSTRUCT>(
@@ -491,8 +539,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       chunk(n_chunks - 1, std::false_type{}, std::false_type{});
     if (MODE == kOutput) {
       const uint32_t last = n_chunks - 1;
-      store_tile<IO, CW>(ro, &st.yo[last & 1][0][0], row_bytes, last * kChunk, steps, valid_bytes,
-                         voff);
+      put_y(last & 1, last * kChunk);
     }
     if (KSTRUCT) {
 #pragma unroll
