@@ -100,6 +100,23 @@ def make_params(w: Workload, device="cpu", seed=0):
     return {"A": A.contiguous(), "D": D, "delta_bias": bias}
 
 
+def make_trained_A(w: Workload, device="cpu", seed=0, spread=0.5, channels=None):
+    """A as it looks after training moved it off the S4D-Real start:
+    A[d, n] = -(n + 1) * f, f log-normal with log-std `spread`, drawn per
+    (channel, state) from its own seeded generator, so that no such channel
+    keeps the A[d, n] = (n + 1) A[d, 0] shape. With `channels` (indices), only
+    those channels are changed and the others keep -(n + 1)."""
+    g = _gen(device, seed + 31337)
+    base = -torch.arange(1, w.dstate + 1, dtype=torch.float32, device=device).repeat(w.dim, 1)
+    f = torch.exp(spread * torch.randn((w.dim, w.dstate), generator=g, device=device))
+    A = base * f
+    if channels is not None:
+        keep = torch.ones(w.dim, dtype=torch.bool, device=device)
+        keep[torch.as_tensor(channels, device=device)] = False
+        A[keep] = base[keep]
+    return A.contiguous()
+
+
 def make_scan_inputs(w: Workload, device="cpu", seed=0):
     """x, delta (Delta_raw), z: (batch, L, dim); B, C: (batch, L, N) in the
     workload's io dtype; plus make_params(). z is None without a gate."""
