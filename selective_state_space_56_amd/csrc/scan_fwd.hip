@@ -29,7 +29,12 @@ namespace mscan {
 
 namespace {
 
-constexpr int kBlock = 256;   // 4 wave64s, one lane per row
+#ifndef MSCAN_BLOCK
+#define MSCAN_BLOCK 256
+#endif
+constexpr int kBlock = MSCAN_BLOCK;  // lanes (channels) per scan workgroup, a multiple of 64
+static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
+constexpr int kAuxBlock = 256;       // threads per workgroup of the small helper kernels
 constexpr int kChunk = 8;     // time steps whose inputs are loaded together
 
 struct Dims {
@@ -148,9 +153,9 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
 // Two buffers: the next chunk is fetched while the current one is computed.
 // With Y, the outputs y of a chunk are collected in LDS and written to HBM as
 // one tile at the start of the next chunk.
-template <int N, class IO, bool Y>
+template <int N, class IO, bool Y, int NIN>
 struct __align__(16) Stage {
-  typename IO::raw in[2][3][kChunk][kBlock];  // [buffer][x, Delta_raw, z][step][channel]
+  typename IO::raw in[2][NIN][kChunk][kBlock];  // [buffer][x, Delta_raw (, z)][step][channel]
   float bc[2][kChunk][2 * N];                 // [buffer][step][B_0..B_{N-1}, C_0..C_{N-1}]
   typename IO::raw yo[Y ? 2 : 1][Y ? kChunk : 1][kBlock];  // [buffer][step][channel]
 };
@@ -333,15 +338,20 @@ enum PathSet { kPathGeneral = 0, kPathStructured = 1, kPathBoth = 2 };
 #ifndef MSCAN_AGG_WAVES
 #define MSCAN_AGG_WAVES 5
 #endif
+#ifndef MSCAN_PIN_STEPS
+#define MSCAN_PIN_STEPS 1
+#endif
 
-// Occupancy targets, in 256-lane workgroups per CU (= waves per SIMD): the
-// output pass stages x, Delta_raw, z and y (35 KB of LDS per workgroup), so at
-// most four fit in a CU's 160 KB; the aggregate pass stages x and Delta_raw
-// only and runs five. The bound keeps the compiler within the matching
-// register budget (128 or 102 vector registers per lane) instead of hoisting
-// loads of later steps.
+// Occupancy targets in waves per SIMD: the output pass stages x, Delta_raw, z
+// and y (35 KB of LDS per 256 lanes), so at most four waves per SIMD fit in a
+// CU's 160 KB; the aggregate pass stages x and Delta_raw only and runs five.
+// The launch bound (in workgroups per CU: four SIMDs per CU) keeps the
+// compiler within the matching register budget (128 or 102 vector registers
+// per lane) instead of hoisting loads of later steps.
 template <int MODE>
-constexpr int kMinBlocksPerCU = MODE == kOutput ? MSCAN_OUT_WAVES : MSCAN_AGG_WAVES;
+constexpr int kWavesPerSimd = MODE == kOutput ? MSCAN_OUT_WAVES : MSCAN_AGG_WAVES;
+template <int MODE>
+constexpr int kMinBlocksPerCU = kWavesPerSimd<MODE> * 4 * 64 / kBlock;
 
 template <int N, class IO, int MODE, bool GATE, int CW, int PATHS>
 __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_kernel(
@@ -356,8 +366,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   constexpr bool kZ = MODE == kOutput && GATE;
   constexpr bool kC = MODE == kOutput;
   constexpr int kTileElems = kChunk * 2 * N;
-  static_assert(kTileElems <= kBlock, "one B/C tile element per thread");
-  __shared__ Stage<N, IO, MODE == kOutput> st;
+  constexpr int kBcPer = (kTileElems + kBlock - 1) / kBlock;  // B/C tile elements per thread
+  __shared__ Stage<N, IO, MODE == kOutput, kZ ? 3 : 2> st;
+  constexpr int kZi = kZ ? 2 : 0;  // z's slot (unused without the gate)
 
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x / g.tiles;
@@ -428,8 +439,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   raw* out0 = out + row0;
   const raw* Bp = B + (b * g.seqlen + t_begin) * N;
   const raw* Cp = C + (b * g.seqlen + t_begin) * N;
-  const BcOffsets bco = bc_offsets<N, IO>(tid);  // this thread's B/C tile element
-  const int bci = tid % kTileElems;
+  // this thread's B/C tile elements: tid, tid + kBlock, ...
+  BcOffsets bco[kBcPer];
+#pragma unroll
+  for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock);
 
   float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta (aggregate mode)
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
@@ -441,17 +454,27 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     if constexpr (CW != 0) {
       dma_tile<IO, CW>(x0 + at, left, row_bytes, &st.in[nb][0][0][0], wv, lane_off);
       dma_tile<IO, CW>(dl0 + at, left, row_bytes, &st.in[nb][1][0][0], wv, lane_off);
-      if (kZ) dma_tile<IO, CW>(z0 + at, left, row_bytes, &st.in[nb][2][0][0], wv, lane_off);
+      if (kZ) dma_tile<IO, CW>(z0 + at, left, row_bytes, &st.in[nb][kZi][0][0], wv, lane_off);
     } else {
       load_tile_regs<IO>(rgx, x0 + at, left, row_bytes, ch_off);
       load_tile_regs<IO>(rgd, dl0 + at, left, row_bytes, ch_off);
       if (kZ) load_tile_regs<IO>(rgz, z0 + at, left, row_bytes, ch_off);
     }
   };
-  // this thread's B/C element of the chunk at step t1
+  // this thread's B/C elements of the chunk at step t1, and their LDS stores
+  float bcv[kBcPer];
   auto fetch_bc = [&](uint32_t t1) {
-    return bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
-                          steps - t1, bco);
+#pragma unroll
+    for (int r = 0; r < kBcPer; ++r)
+      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
+                              steps - t1, bco[r]);
+  };
+  auto land_bc = [&](int nb) {
+#pragma unroll
+    for (int r = 0; r < kBcPer; ++r) {
+      const int i = tid + r * kBlock;
+      if (i < kTileElems) st.bc[nb][i / (2 * N)][i % (2 * N)] = bcv[r];
+    }
   };
   // y tile of the chunk at step t1 from LDS buffer yb to HBM
   auto put_y = [&](int yb, uint32_t t1) {
@@ -462,7 +485,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     if constexpr (CW == 0) {
       store_tile_regs<IO>(rgx, &st.in[nb][0][0][0]);
       store_tile_regs<IO>(rgd, &st.in[nb][1][0][0]);
-      if (kZ) store_tile_regs<IO>(rgz, &st.in[nb][2][0][0]);
+      if (kZ) store_tile_regs<IO>(rgz, &st.in[nb][kZi][0][0]);
     }
   };
   // The whole segment, for S4D-Real-shaped tiles (powers of one decay) or
@@ -472,9 +495,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     float dx_prev = 1.0f;  // structured rows: h holds g = h / dx_prev
     // chunk 0 into buffer 0
     fetch(0, 0);
-    float bcv = fetch_bc(0);
+    fetch_bc(0);
     land(0);
-    if (tid < kTileElems) st.bc[0][bci / (2 * N)][bci % (2 * N)] = bcv;
+    land_bc(0);
     wait_vmem();
     __syncthreads();
     const uint32_t n_chunks = (steps + kChunk - 1) / kChunk;
@@ -490,11 +513,11 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
         put_y(buf ^ 1, t0 - kChunk);
       if (MORE) {
         fetch(buf ^ 1, t0 + kChunk);
-        bcv = fetch_bc(t0 + kChunk);
+        fetch_bc(t0 + kChunk);
       }
       const int valid = FULL ? kChunk : static_cast<int>(steps - t0);
       FrontEnd fe = front_end<N, IO, MODE, GATE, KSTRUCT>(
-          st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][2][0][tid] : raw(0), A2[0],
+          st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][kZi][0][tid] : raw(0), A2[0],
           bias);
       float dsum = 0.0f;  // this chunk's Delta (aggregate mode)
 #pragma unroll
@@ -505,7 +528,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           if (j + 1 < kChunk && (FULL || j + 1 < valid))
             fn = front_end<N, IO, MODE, GATE, KSTRUCT>(
                 st.in[buf][0][js + 1][tid], st.in[buf][1][js + 1][tid],
-                kZ ? st.in[buf][2][js + 1][tid] : raw(0), A2[0], bias);
+                kZ ? st.in[buf][kZi][js + 1][tid] : raw(0), A2[0], bias);
           float bc[2 * N];
           read_bc<N>(st.bc[buf][js], bc, kC);
           const raw y = update<N, IO, MODE, GATE, KSTRUCT>(fe, bc, A2, Dd, h, dx_prev);
@@ -515,8 +538,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           // This step's state update completes here, not after later steps'
           // loads (in the aggregate pass nothing else uses it, and hoisted
           // loads would only hold registers).
+#if MSCAN_PIN_STEPS
 #pragma unroll
           for (int n = 0; n < N; ++n) asm volatile("" : "+v"(h[n]));
+#endif
         }
       }
       if (MODE == kAggregate) {
@@ -527,7 +552,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       }
       if (MORE) {
         land(buf ^ 1);
-        if (tid < kTileElems) st.bc[buf ^ 1][bci / (2 * N)][bci % (2 * N)] = bcv;
+        land_bc(buf ^ 1);
         wait_vmem();
       }
       __syncthreads();
@@ -577,12 +602,12 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
 constexpr int kFoldBlock = 8;
 
 template <int N>
-__global__ __launch_bounds__(kBlock) void scan_combine_kernel(const float* __restrict__ A,
+__global__ __launch_bounds__(kAuxBlock) void scan_combine_kernel(const float* __restrict__ A,
                                                               float* __restrict__ ws_h,
                                                               const float* __restrict__ ws_s,
                                                               int64_t rows, int64_t dim,
                                                               int segments) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
   if (i >= rows * N) return;
   const int64_t row = i / N;
   const int n = static_cast<int>(i % N);
@@ -608,8 +633,8 @@ __global__ __launch_bounds__(kBlock) void scan_combine_kernel(const float* __res
   }
 }
 
-__global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* p, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+__global__ __launch_bounds__(kAuxBlock) void fill_zero_kernel(float* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
   if (i < n) p[i] = 0.0f;
 }
 
@@ -651,8 +676,8 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
                          grid_agg, block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out,
                          p.last_state, ws_h, ws_s, g);
     const int64_t work = g.rows * N;
-    const dim3 grid_c(static_cast<unsigned>((work + kBlock - 1) / kBlock));
-    hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, block, 0, stream, p.A, ws_h, ws_s,
+    const dim3 grid_c(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock));
+    hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s,
                        g.rows, p.dim, plan.segments);
   }
   const dim3 grid(blocks, plan.segments);
@@ -767,8 +792,9 @@ hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* wor
   if (p.seqlen == 0) {
     if (p.last_state) {
       const int64_t n = p.batch * p.dim * p.dstate;
-      hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + kBlock - 1) / kBlock)),
-                         dim3(kBlock), 0, stream, p.last_state, n);
+      hipLaunchKernelGGL(fill_zero_kernel,
+                         dim3(static_cast<unsigned>((n + kAuxBlock - 1) / kAuxBlock)),
+                         dim3(kAuxBlock), 0, stream, p.last_state, n);
       return hipGetLastError();
     }
     return hipSuccess;
