@@ -110,9 +110,22 @@ def time_calls(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, nthreads):
-    """The fp64 oracle on the whole workload, on this host's cores."""
-    import numpy as np  # noqa: F401
+    """The fp64 oracle on the whole workload on this host's cores, and on one
+    thread over every 16th channel (rows are independent, so the work scales
+    exactly with the channel count)."""
+    import numpy as np
     from oracle import default_oracle
     from selective_state_space_56_amd.workloads import to_f64_numpy
     orc = default_oracle()
@@ -121,9 +134,28 @@ def cpu_baseline(w, inp, nthreads):
     t0 = time.perf_counter()
     orc.scan(*args, **kw, nthreads=nthreads)
     dt = time.perf_counter() - t0
+    ch = np.arange(0, w.dim, 16)
+    sub = [np.ascontiguousarray(args[0][:, :, ch]), np.ascontiguousarray(args[1][:, :, ch]),
+           np.ascontiguousarray(args[2][ch]), args[3], args[4]]
+    skw = {"D": np.ascontiguousarray(kw["D"][ch]), "z": np.ascontiguousarray(kw["z"][:, :, ch]),
+           "delta_bias": np.ascontiguousarray(kw["delta_bias"][ch])}
+    t1 = time.perf_counter()
+    orc.scan(*sub, **skw, nthreads=1)
+    dt1 = time.perf_counter() - t1
+    one = w.batch * w.seqlen * len(ch) / dt1
     return {"value": w.elem_steps / dt, "unit": "elem-steps/s", "cores": nthreads, "kind": "oracle",
             "sample": f"whole workload ({w.batch}x{w.seqlen}x{w.dim}, N={w.dstate}), fp64, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall on {nthreads} threads; one thread on every 16th channel: "
+                      f"{one:.3g} elem-steps/s ({dt1:.2f} s)",
+            "single_thread_value": one, "cpu_model": cpu_model()}
+
+
+def call_stats(ms):
+    """median, min and interquartile range of per-call times (ms)."""
+    import numpy as np
+    q1, med, q3 = np.percentile(ms, [25, 50, 75])
+    return {"median_launch_ms": float(med), "min_launch_ms": float(min(ms)),
+            "iqr_launch_ms": [float(q1), float(q3)]}
 
 
 def main():
@@ -216,10 +248,11 @@ def main():
                      "traffic": recorded_traffic("scan", w.name),
                      "kernel": "mamba_scan_fwd call (aggregate, fold and output kernels)",
                      "algorithmic_flops_per_launch": nflops, "avg_launch_ms": kern_ms,
-                     "min_launch_ms": min(per_call), "workspace_bytes": ws_bytes,
+                     **call_stats(per_call), "workspace_bytes": ws_bytes,
                      "published_fp32_vector_peak": PUBLISHED_FP32_VECTOR_TFLOPS},
         "hbm": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes},
+                "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                "achieved_at_median": nbytes / (call_stats(per_call)["median_launch_ms"] * 1e-3) / 1e9},
     }
 
     if not args.no_decode:
@@ -247,7 +280,7 @@ def main():
         rec["decode"] = {
             "workload": wd.name, "steps": wd.decode_steps, "ms_total": dt * 1e3,
             "value": wd.batch * wd.dim * wd.decode_steps / dt, "unit": "elem-steps/s",
-            "avg_launch_ms": dms,
+            "avg_launch_ms": dms, **call_stats(dcalls),
             "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": recorded_traffic("decode", wd.name),
