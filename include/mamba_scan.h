@@ -119,6 +119,26 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc *desc, const void *x,
                             size_t workspace_bytes, void *stream);
 
 /*
+ * mamba_scan_fwd from a given initial state instead of zeros: the state
+ * before the first step is h0 ("State space models and Mamba", "A worked
+ * example" and the convolution view: the state carries everything earlier
+ * input contributed, so a sequence scanned in pieces, each piece starting from
+ * the previous piece's final state, gives the result of one scan over the
+ * whole sequence).
+ *   h0 : (batch, dim, dstate) float32, 4-byte aligned, or NULL (zeros, the
+ *        same as mamba_scan_fwd). Read only; it must not overlap out,
+ *        last_state or the workspace (so one call's last_state cannot be its
+ *        own h0: pass a copy). With seqlen == 0, last_state receives h0.
+ * All other arguments, sizes, workspace and errors as mamba_scan_fwd.
+ */
+mamba_status mamba_scan_fwd_init(const mamba_scan_desc *desc, const void *x,
+                                 const void *delta, const float *A, const void *B,
+                                 const void *C, const float *D, const void *z,
+                                 const float *delta_bias, const float *h0,
+                                 void *out, float *last_state, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
  * One decode token for every sequence, against a resident state
  * (desc->seqlen must be 1).
  *   state       : (batch, dim, dstate) float32, read and overwritten in place

@@ -57,6 +57,9 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_scan_fwd.restype = ctypes.c_int
         lib.mamba_scan_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, vp, fp,
                                        vp, sz, vp]
+        lib.mamba_scan_fwd_init.restype = ctypes.c_int
+        lib.mamba_scan_fwd_init.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, fp,
+                                            vp, fp, vp, sz, vp]
         lib.mamba_state_update.restype = ctypes.c_int
         lib.mamba_state_update.argtypes = [ctypes.POINTER(Desc), fp, vp, vp, fp, vp, vp, fp, vp, fp,
                                            vp, vp]
@@ -103,15 +106,17 @@ def workspace_size(batch, seqlen, dim, dstate, io_dtype=torch.bfloat16, segments
     return int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
 
 
-def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None, last_state=None,
-             return_last_state=True, segments=0):
+def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out=None,
+             last_state=None, return_last_state=True, segments=0):
     """Selective scan over full sequences.
 
     x, delta (Delta_raw), z: (batch, L, dim) float32 or bfloat16 on a GPU;
     A: (dim, N) float32; B, C: (batch, L, N) in x's dtype; D, delta_bias:
-    (dim,) float32 or None. Returns (out, last_state) where out is
-    (batch, L, dim) in x's dtype and last_state (batch, dim, N) float32 (None
-    if not requested). ``segments`` > 0 forces the number of time segments.
+    (dim,) float32 or None; h0: (batch, dim, N) float32 initial state or None
+    (zeros; with h0 the call goes to mamba_scan_fwd_init). Returns
+    (out, last_state) where out is (batch, L, dim) in x's dtype and last_state
+    (batch, dim, N) float32 (None if not requested). ``segments`` > 0 forces
+    the number of time segments.
     """
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
@@ -132,6 +137,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None, la
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     _need(x, "x", (batch, L, dim), io, dev)
+    _need(h0, "h0", (batch, dim, N), torch.float32, dev)
     if out is None:
         out = torch.empty((batch, L, dim), dtype=io, device=dev)
     _need(out, "out", (batch, L, dim), io, dev)
@@ -141,9 +147,15 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None, la
     d = Desc(batch, L, dim, N, _IO[io], int(segments))
     ws_bytes = int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = lib.mamba_scan_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                            _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out), _ptr(last_state),
-                            _ptr(ws), ctypes.c_size_t(ws_bytes), _stream(dev))
+    if h0 is None:
+        st = lib.mamba_scan_fwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out), _ptr(last_state),
+                                _ptr(ws), ctypes.c_size_t(ws_bytes), _stream(dev))
+    else:
+        st = lib.mamba_scan_fwd_init(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0),
+                                     _ptr(out), _ptr(last_state), _ptr(ws),
+                                     ctypes.c_size_t(ws_bytes), _stream(dev))
     _check(lib, st)
     return out, last_state
 

@@ -97,11 +97,15 @@ size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
       .workspace_bytes;
 }
 
-mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void* delta,
-                            const float* A, const void* B, const void* C, const float* D,
-                            const void* z, const float* delta_bias, void* out, float* last_state,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  const char* who = "mamba_scan_fwd";
+}  // extern "C"
+
+namespace {
+
+mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void* x,
+                           const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, const float* h0,
+                           void* out, float* last_state, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
   if (d->flags & ~0xffffu)
@@ -151,6 +155,9 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
     if (overlaps(o_ws, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace overlaps %s", who, s.name);
   }
   if (overlaps(o_out, o_last)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps last_state", who);
+  const Span i_h0{"h0", h0, static_cast<size_t>(rows) * N * 4};
+  if (overlaps(i_h0, o_out) || overlaps(i_h0, o_last) || overlaps(i_h0, o_ws))
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: h0 overlaps out, last_state or the workspace", who);
   if (overlaps(o_ws, o_out) || overlaps(o_ws, o_last))
     return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace overlaps an output", who);
   const size_t align = eb;
@@ -163,7 +170,8 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
     if (s.p && reinterpret_cast<uintptr_t>(s.p) % bc_align)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, bc_align);
   for (const void* p : {static_cast<const void*>(A), static_cast<const void*>(D),
-                        static_cast<const void*>(delta_bias), static_cast<const void*>(last_state)})
+                        static_cast<const void*>(delta_bias), static_cast<const void*>(last_state),
+                        static_cast<const void*>(h0)})
     if (p && reinterpret_cast<uintptr_t>(p) % 4)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: an fp32 argument is not 4-byte aligned", who);
 
@@ -178,6 +186,7 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
   p.D = D;
   p.z = z;
   p.bias = delta_bias;
+  p.h0 = h0;
   p.out = out;
   p.last_state = last_state;
   p.batch = d->batch;
@@ -189,6 +198,27 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void* delta,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias, void* out, float* last_state,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_fwd_impl("mamba_scan_fwd", d, x, delta, A, B, C, D, z, delta_bias, nullptr, out,
+                       last_state, workspace, workspace_bytes, stream);
+}
+
+mamba_status mamba_scan_fwd_init(const mamba_scan_desc* d, const void* x, const void* delta,
+                                 const float* A, const void* B, const void* C, const float* D,
+                                 const void* z, const float* delta_bias, const float* h0,
+                                 void* out, float* last_state, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return scan_fwd_impl("mamba_scan_fwd_init", d, x, delta, A, B, C, D, z, delta_bias, h0, out,
+                       last_state, workspace, workspace_bytes, stream);
 }
 
 mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const void* x,

@@ -18,6 +18,7 @@ struct ScanProblem {
   const float* D;      // nullable
   const void* z;       // nullable
   const float* bias;   // nullable
+  const float* h0;     // nullable (zeros): state before the first step
   void* out;
   float* last_state;   // nullable
   int64_t batch, seqlen, dim;

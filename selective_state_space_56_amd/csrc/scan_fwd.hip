@@ -15,7 +15,8 @@
 //   1. aggregate: each segment but the last scans from h = 0 and records its
 //      end state and the sum of its Delta (the segment's decay for state n is
 //      exp(A_n * sum Delta), a product of per-step decays);
-//   2. combine: a sequential fold over segments per (row, n) turns the
+//   2. combine: a sequential fold over segments per (row, n), from the initial
+//      state (zero, or the caller's h0), turns the
 //      aggregates into each segment's carry-in state;
 //   3. output: every segment re-scans from its carry-in and writes y (and the
 //      last one the final state).
@@ -45,6 +46,7 @@ struct Dims {
   int segments;
   unsigned tiles;   // channel tiles of kBlock per batch row
   uint32_t* tile_flags;  // per channel tile: 1 = S4D-Real shaped (workspace), or null
+  const float* h0;       // state before the first step, (batch, dim, N), or null (zeros)
 };
 
 enum Mode { kOutput = 0, kAggregate = 1 };
@@ -413,8 +415,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const float bias = bias_p ? bias_p[d] : 0.0f;
 
   float h[N];
-  if (MODE == kOutput && s > 0) {
-    const float* hin = ws_h + (static_cast<int64_t>(s - 1) * g.rows + row) * N;
+  if (MODE == kOutput && (s > 0 || g.h0 != nullptr)) {
+    // carry-in: the folded state after segment s - 1, or the initial state
+    const float* hin = s > 0 ? ws_h + (static_cast<int64_t>(s - 1) * g.rows + row) * N
+                             : g.h0 + row * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = hin[n];
   } else {
@@ -594,9 +598,10 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   }
 }
 
-// Fold the segment aggregates of one (row, n) in time order. Slot k of the
-// workspace holds segment k's (end state from zero, sum of Delta) on entry and
-// the carry-in state of segment k + 1 on exit. The slots are read in blocks of
+// Fold the segment aggregates of one (row, n) in time order, starting from the
+// initial state (h0, or zero). Slot k of the workspace holds segment k's (end
+// state from zero, sum of Delta) on entry and the carry-in state of segment
+// k + 1 on exit. The slots are read in blocks of
 // kFoldBlock before they are folded and written, so the loads of a block are
 // in flight together.
 constexpr int kFoldBlock = 8;
@@ -605,6 +610,7 @@ template <int N>
 __global__ __launch_bounds__(kAuxBlock) void scan_combine_kernel(const float* __restrict__ A,
                                                               float* __restrict__ ws_h,
                                                               const float* __restrict__ ws_s,
+                                                              const float* __restrict__ h0,
                                                               int64_t rows, int64_t dim,
                                                               int segments) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(kAuxBlock) void scan_combine_kernel(const float* __
   const int64_t d = row % dim;
   const float a2 = A[d * N + n] * kLog2e;
   const int aggs = segments - 1;
-  float h = 0.0f;
+  float h = h0 ? h0[i] : 0.0f;
   for (int k0 = 0; k0 < aggs; k0 += kFoldBlock) {
     float hv[kFoldBlock], sv[kFoldBlock];
 #pragma unroll
@@ -633,9 +639,11 @@ __global__ __launch_bounds__(kAuxBlock) void scan_combine_kernel(const float* __
   }
 }
 
-__global__ __launch_bounds__(kAuxBlock) void fill_zero_kernel(float* p, int64_t n) {
+// dst[i] = src[i] (or 0 without src): the final state of an empty sequence
+__global__ __launch_bounds__(kAuxBlock) void init_state_kernel(float* dst, const float* src,
+                                                               int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
 template <int N, class IO, int CW>
@@ -649,6 +657,7 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.seg_len = plan.seg_len;
   g.segments = plan.segments;
   g.tiles = static_cast<unsigned>((p.dim + kBlock - 1) / kBlock);
+  g.h0 = p.h0;
   float* ws_h = static_cast<float*>(workspace);
   float* ws_s = ws_h ? ws_h + static_cast<int64_t>(plan.segments - 1) * g.rows * N : nullptr;
   g.tile_flags = ws_s ? reinterpret_cast<uint32_t*>(ws_s + static_cast<int64_t>(plan.segments - 1) *
@@ -678,7 +687,7 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
     const int64_t work = g.rows * N;
     const dim3 grid_c(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock));
     hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s,
-                       g.rows, p.dim, plan.segments);
+                       p.h0, g.rows, p.dim, plan.segments);
   }
   const dim3 grid(blocks, plan.segments);
   if (z) {
@@ -792,9 +801,9 @@ hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* wor
   if (p.seqlen == 0) {
     if (p.last_state) {
       const int64_t n = p.batch * p.dim * p.dstate;
-      hipLaunchKernelGGL(fill_zero_kernel,
+      hipLaunchKernelGGL(init_state_kernel,
                          dim3(static_cast<unsigned>((n + kAuxBlock - 1) / kAuxBlock)),
-                         dim3(kAuxBlock), 0, stream, p.last_state, n);
+                         dim3(kAuxBlock), 0, stream, p.last_state, p.h0, n);
       return hipGetLastError();
     }
     return hipSuccess;

@@ -35,15 +35,17 @@ def to_dev(inp, device="cuda"):
     return {k: (None if v is None else v.to(device)) for k, v in inp.items()}
 
 
-def gpu_scan(inp, segments=0, with_D=True, with_z=True, with_bias=True):
+def gpu_scan(inp, segments=0, with_D=True, with_z=True, with_bias=True, h0=None):
     out, last = scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"],
                          D=inp["D"] if with_D else None, z=inp["z"] if with_z else None,
-                         delta_bias=inp["delta_bias"] if with_bias else None, segments=segments)
+                         delta_bias=inp["delta_bias"] if with_bias else None, h0=h0,
+                         segments=segments)
     torch.cuda.synchronize()
     return out, last
 
 
-def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=True, nthreads=None):
+def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=True, nthreads=None,
+                h0=None):
     """Run the oracle on the exact stored inputs (optionally only on a subset
     of channels; rows are independent, so that is the same computation)."""
     def sl(t, dim_axis):
@@ -57,7 +59,8 @@ def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=Tru
     return orc.scan(sl(inp["x"], 2), sl(inp["delta"], 2), A, to_f64_numpy(inp["B"]),
                     to_f64_numpy(inp["C"]), D=sl(inp["D"], 0) if with_D else None,
                     z=sl(inp["z"], 2) if with_z else None,
-                    delta_bias=sl(inp["delta_bias"], 0) if with_bias else None, nthreads=nthreads)
+                    delta_bias=sl(inp["delta_bias"], 0) if with_bias else None,
+                    h0=sl(h0, 1), nthreads=nthreads)
 
 
 def gpu_decode(state, tok, params):

@@ -32,8 +32,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_state_update",
-                          "mamba_status_string", "mamba_last_error"}
+    assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_init",
+                          "mamba_state_update", "mamba_status_string", "mamba_last_error"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -59,6 +59,31 @@ def scan(lib, desc, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, out=9, last=1
     w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
     return lib.mamba_scan_fwd(None if desc is None else ctypes.byref(desc), *ptrs, w,
                               ctypes.c_size_t(ws_bytes), None)
+
+
+def scan_init(lib, desc, h0, out=9, last=10, ws=None, ws_bytes=0):
+    args = [1, 2, 3, 4, 5, 6, 7, 8, h0, out, last]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
+    return lib.mamba_scan_fwd_init(ctypes.byref(desc), *ptrs, w, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_scan_init_validates_h0(lib):
+    d = D_()
+    assert scan_init(lib, d, h0=9) == INVALID               # h0 == out
+    assert "h0 overlaps" in err(lib)
+    assert scan_init(lib, d, h0=10) == INVALID              # h0 == last_state
+    assert "h0 overlaps" in err(lib)
+    odd = ctypes.c_void_p(FAKE + 0x100000 * 12 + 2)
+    assert scan_init(lib, d, h0=odd) == INVALID
+    assert "aligned" in err(lib)
+    dw = D_(batch=1, seqlen=64, dim=16, flags=4)
+    need = lib.mamba_scan_workspace_size(ctypes.byref(dw))
+    assert scan_init(lib, dw, h0=20, ws=20, ws_bytes=need) == INVALID   # h0 == workspace
+    assert "h0 overlaps" in err(lib)
+    # the common checks run as for mamba_scan_fwd, under this entry point's name
+    assert lib.mamba_scan_fwd_init(None, *([None] * 12), ctypes.c_size_t(0), None) == INVALID
+    assert "mamba_scan_fwd_init: desc is NULL" in err(lib)
 
 
 def upd(lib, desc, state=11, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, out=9):

@@ -115,6 +115,51 @@ def test_mixed_tiles(orc, dev, io):
         _check_scan(orc, w, inp, segments=segments)
 
 
+@pytest.mark.parametrize("io,general,segments", [
+    ("f32", False, 1), ("f32", False, 0), ("bf16", False, 7), ("f32", True, 0), ("bf16", True, 1),
+])
+def test_initial_state(orc, dev, io, general, segments):
+    """mamba_scan_fwd_init: the scan from a given state h0 ~ N(0, 1)."""
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="h0", batch=2, seqlen=500, dim=300, io=io)
+    _say(f"case initial state {io} general={general} seg={segments}")
+    inp = make_scan_inputs(w, seed=21)
+    if general:
+        inp["A"] = make_trained_A(w, seed=21)
+    inp = to_dev(inp, dev)
+    h0 = make_decode_state(w, device=dev, seed=21)
+    _check_scan(orc, w, inp, segments=segments, h0=h0)
+
+
+def test_scan_in_pieces(orc, dev):
+    """A sequence scanned in three calls, each from the previous call's final
+    state, gives the one-call scan ("State space models and Mamba": the state
+    carries all earlier input)."""
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="pieces", batch=2, seqlen=1200, dim=520,
+                                                 io="f32")
+    inp = to_dev(make_scan_inputs(w, seed=22), dev)
+    y_all, h_all = gpu_scan(inp)
+    cuts = [0, 333, 800, 1200]
+    ys, h = [], None
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = {k: (v[:, a:b].contiguous() if k in ("x", "delta", "z", "B", "C") else v)
+                for k, v in inp.items()}
+        y, h = gpu_scan(part, h0=h)
+        ys.append(y)
+    y_cat = torch.cat(ys, dim=1)
+    ey = norm_err(to_f64_numpy(y_cat), to_f64_numpy(y_all))
+    eh = norm_err(to_f64_numpy(h), to_f64_numpy(h_all))
+    _say(f"scan in pieces: err(y)={ey:.3e} err(state)={eh:.3e}")
+    assert ey < 1e-5 and eh < 1e-5
+
+
+def test_initial_state_empty_sequence(dev):
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="h0empty", batch=2, seqlen=0, dim=40)
+    inp = to_dev(make_scan_inputs(w), dev)
+    h0 = make_decode_state(w, device=dev, seed=5)
+    out, last = gpu_scan(inp, h0=h0)
+    assert out.shape == (2, 0, 40) and torch.equal(last, h0)
+
+
 def test_optional_arguments_absent(orc, dev):
     w = WORKLOADS["mamba130m_layer"].with_shape(name="noopt", batch=2, seqlen=300, dim=96)
     _say("case optional arguments absent")
