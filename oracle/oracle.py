@@ -58,6 +58,10 @@ class Oracle:
         lib.oracle_state_update_f64.restype = ctypes.c_int
         lib.oracle_state_update_f64.argtypes = [_i64, _i64, _i64] + [_dp] * 9 + \
             [ctypes.c_int, _dp, ctypes.c_int]
+        lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
+        lib.oracle_conv1d_silu_f64.argtypes = [_i64] * 4 + [_dp] * 6 + [ctypes.c_int]
+        lib.oracle_conv1d_update_f64.restype = ctypes.c_int
+        lib.oracle_conv1d_update_f64.argtypes = [_i64] * 3 + [_dp] * 5 + [ctypes.c_int]
         self.lib = lib
 
     def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
@@ -108,6 +112,43 @@ class Oracle:
                                               _ptr(delta_bias), int(bool(zoh)), _ptr(out), nt)
         if rc != 0:
             raise ValueError("oracle_state_update_f64 returned %d" % rc)
+        return out, st
+
+
+    def conv1d(self, xin, weight, bias=None, state_in=None, nthreads=None):
+        """Causal depthwise convolution + SiLU. xin: (batch, L, dim); weight:
+        (dim, width); bias: (dim,); state_in: (batch, dim, width - 1). Returns
+        (out (batch, L, dim), state_out (batch, dim, width - 1))."""
+        xin = _f64(xin)
+        batch, L, dim = xin.shape
+        weight = _f64(weight)
+        width = weight.shape[1]
+        bias = _f64(bias, (dim,))
+        state_in = _f64(state_in, (batch, dim, width - 1))
+        out = np.empty((batch, L, dim), dtype=np.float64)
+        st = np.empty((batch, dim, width - 1), dtype=np.float64)
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_conv1d_silu_f64(batch, L, dim, width, _ptr(xin), _ptr(weight),
+                                             _ptr(bias), _ptr(state_in), _ptr(out), _ptr(st), nt)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_silu_f64 returned %d" % rc)
+        return out, st
+
+    def conv1d_update(self, state, xin, weight, bias=None, nthreads=None):
+        """One token: state (batch, dim, width - 1), updated copy returned; xin
+        (batch, dim). Returns (out (batch, dim), new_state)."""
+        xin = _f64(xin)
+        batch, dim = xin.shape
+        weight = _f64(weight)
+        width = weight.shape[1]
+        st = np.array(_f64(state, (batch, dim, width - 1)), dtype=np.float64, copy=True)
+        bias = _f64(bias, (dim,))
+        out = np.empty((batch, dim), dtype=np.float64)
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_conv1d_update_f64(batch, dim, width, _ptr(st), _ptr(xin),
+                                               _ptr(weight), _ptr(bias), _ptr(out), nt)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_update_f64 returned %d" % rc)
         return out, st
 
 

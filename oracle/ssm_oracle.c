@@ -153,3 +153,87 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate,
   }
   return 0;
 }
+
+/*
+ * Causal depthwise convolution followed by SiLU: the front-end of the SSM
+ * branch (ai.thesatyajit.com, "The Mamba block": a causal depthwise
+ * convolution of width 4, then SiLU, then the selective SSM; erikxu.me notes,
+ * "Mamba": the short depthwise convolution mixes nearby sequence positions
+ * within each channel, then SiLU, then the SSM).
+ *
+ * For every batch row b and channel d independently, with the inputs before
+ * t = 0 taken from state_in (the last width - 1 inputs of an earlier piece of
+ * the sequence, oldest first; zeros without it):
+ *   v_t = bias[d] + sum_{j=0}^{width-1} weight[d, j] * xin[b, t - (width-1) + j, d]
+ *   out[b, t, d] = silu(v_t)
+ * so weight[d, width - 1] multiplies the current input (the tap order of a
+ * causal Conv1d padded by width - 1 steps on the left).
+ * state_out[b, d, j] = xin[b, seqlen - (width-1) + j, d] for j < width - 1
+ * (taken from state_in where that time index is negative): what a later
+ * piece, or the one-token update, needs.
+ * Layouts: xin, out: (batch, seqlen, dim); weight: (dim, width); bias: (dim);
+ * state_in, state_out: (batch, dim, width - 1).
+ */
+static double conv_input(const double *xin, const double *state_in, int64_t seqlen,
+                         int64_t dim, int64_t width, int64_t b, int64_t d, int64_t t) {
+  if (t >= 0) return xin[(b * seqlen + t) * dim + d];
+  if (!state_in) return 0.0;
+  return state_in[(b * dim + d) * (width - 1) + (width - 1) + t];
+}
+
+int oracle_conv1d_silu_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                           const double *xin, const double *weight, const double *bias,
+                           const double *state_in, double *out, double *state_out,
+                           int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || width < 1) return -1;
+  if ((batch * seqlen * dim > 0) && (!xin || !out || !weight)) return -1;
+  if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double v = bias ? bias[d] : 0.0;
+        for (int64_t j = 0; j < width; ++j)
+          v += weight[d * width + j] *
+               conv_input(xin, state_in, seqlen, dim, width, b, d, t - (width - 1) + j);
+        out[(b * seqlen + t) * dim + d] = silu(v);
+      }
+      if (state_out)
+        for (int64_t j = 0; j < width - 1; ++j)
+          state_out[(b * dim + d) * (width - 1) + j] =
+              conv_input(xin, state_in, seqlen, dim, width, b, d, seqlen - (width - 1) + j);
+    }
+  }
+  return 0;
+}
+
+/*
+ * One token of the convolution against its state (the decode step): the
+ * state holds the last width - 1 inputs, oldest first; the output uses them
+ * and the new input, then the state shifts by one and takes the new input.
+ * state: (batch, dim, width - 1), read and written in place; xin, out:
+ * (batch, dim).
+ */
+int oracle_conv1d_update_f64(int64_t batch, int64_t dim, int64_t width, double *state,
+                             const double *xin, const double *weight, const double *bias,
+                             double *out, int nthreads) {
+  if (batch < 0 || dim < 0 || width < 1) return -1;
+  if ((batch * dim > 0) && (!xin || !out || !weight || (width > 1 && !state))) return -1;
+  if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double *s = state ? state + (b * dim + d) * (width - 1) : NULL;
+      const double *w = weight + d * width;
+      double v = bias ? bias[d] : 0.0;
+      for (int64_t j = 0; j < width - 1; ++j) v += w[j] * s[j];
+      v += w[width - 1] * xin[b * dim + d];
+      out[b * dim + d] = silu(v);
+      for (int64_t j = 0; j + 1 < width - 1; ++j) s[j] = s[j + 1];
+      if (width > 1) s[width - 2] = xin[b * dim + d];
+    }
+  }
+  return 0;
+}

@@ -459,6 +459,106 @@ def pin_decode_equals_scan(orc):
     _close(h1, h_full, 1e-13, 1e-15, "prefill + decode state")
 
 
+# ---------------------------------------------------------------------------
+# Causal depthwise convolution + SiLU (the SSM branch's front-end:
+# ai.thesatyajit.com, "The Mamba block"; erikxu.me notes, "Mamba")
+# ---------------------------------------------------------------------------
+
+def _silu(v):
+    return v * _sigmoid(v)
+
+
+def pin_conv_impulse(orc):
+    """A unit impulse at t0 in one channel gives silu(bias + w[W-1-k]) at
+    t0 + k for k < W and silu(bias) elsewhere: the current input meets the
+    last tap, and the filter never looks ahead (causal)."""
+    W, L, t0 = 4, 12, 5
+    w = np.array([[0.5, -1.5, 2.0, 3.0], [0.25, 0.5, -0.75, 1.25]])
+    bias = np.array([0.0, -0.3])
+    x = np.zeros((1, L, 2))
+    x[0, t0, 1] = 1.0
+    out, _ = orc.conv1d(x, w, bias)
+    want = np.full(L, _silu(bias[1]))
+    for k in range(W):
+        want[t0 + k] = _silu(bias[1] + w[1, W - 1 - k])
+    _close(out[0, :, 1], want, 1e-15, 1e-15, "impulse, channel 1")
+    _close(out[0, :, 0], np.zeros(L), 0, 0, "silent channel")
+
+
+def pin_conv_matches_library_convolution(orc):
+    """Per channel, the pre-activation is numpy's full discrete convolution of
+    the input with the reversed taps, truncated to the first L outputs."""
+    rng = np.random.default_rng(31)
+    for W in (4, 3, 2, 1):
+        x = rng.normal(size=(2, 37, 5))
+        w = rng.normal(size=(5, W))
+        bias = rng.normal(size=5)
+        out, _ = orc.conv1d(x, w, bias)
+        want = np.empty_like(out)
+        for b in range(2):
+            for d in range(5):
+                pre = np.convolve(x[b, :, d], w[d, ::-1])[:37] + bias[d]
+                want[b, :, d] = _silu(pre)
+        _close(out, want, 1e-13, 1e-14, f"np.convolve, width {W}")
+
+
+def pin_conv_pieces(orc):
+    """A sequence convolved in pieces, each starting from the previous piece's
+    state (its last W - 1 inputs), gives the one-piece result."""
+    rng = np.random.default_rng(32)
+    x = rng.normal(size=(2, 40, 6))
+    w = rng.normal(size=(6, 4))
+    bias = rng.normal(size=6)
+    s0 = rng.normal(size=(2, 6, 3))
+    whole, s_whole = orc.conv1d(x, w, bias, state_in=s0)
+    outs, st = [], s0
+    for a, b in [(0, 1), (1, 2), (2, 17), (17, 40)]:
+        o, st = orc.conv1d(x[:, a:b], w, bias, state_in=st)
+        outs.append(o)
+    _close(np.concatenate(outs, axis=1), whole, 1e-14, 1e-15, "pieces")
+    _close(st, s_whole, 0, 0, "final state")
+    _close(s_whole, x[:, -3:].transpose(0, 2, 1), 0, 0, "state = last three inputs")
+
+
+def pin_conv_short_sequence_state(orc):
+    """With fewer than W - 1 new inputs the returned state still holds the
+    last W - 1 inputs overall, oldest first: the older ones from the given
+    state, then the new ones."""
+    rng = np.random.default_rng(33)
+    s0 = rng.normal(size=(1, 3, 3))
+    x = rng.normal(size=(1, 2, 3))
+    _, st = orc.conv1d(x, rng.normal(size=(3, 4)), state_in=s0)
+    want = np.concatenate([s0, x.transpose(0, 2, 1)], axis=2)[:, :, -3:]
+    _close(st, want, 0, 0, "short-sequence state")
+    _, st0 = orc.conv1d(np.zeros((1, 0, 3)), rng.normal(size=(3, 4)), state_in=s0)
+    _close(st0, s0, 0, 0, "empty sequence keeps the state")
+
+
+def pin_conv_update_equals_conv(orc):
+    """The one-token update (state shift register) applied L times gives the
+    sequence convolution and its final state."""
+    rng = np.random.default_rng(34)
+    x = rng.normal(size=(3, 9, 4))
+    w = rng.normal(size=(4, 4))
+    bias = rng.normal(size=4)
+    s0 = rng.normal(size=(3, 4, 3))
+    whole, s_whole = orc.conv1d(x, w, bias, state_in=s0)
+    st = s0
+    for t in range(9):
+        o, st = orc.conv1d_update(st, x[:, t], w, bias)
+        _close(o, whole[:, t], 1e-14, 1e-15, f"update step {t}")
+    _close(st, s_whole, 0, 0, "update final state")
+
+
+CONV_PINS = [
+    pin_conv_impulse,
+    pin_conv_matches_library_convolution,
+    pin_conv_pieces,
+    pin_conv_short_sequence_state,
+    pin_conv_update_equals_conv,
+]
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_gated_rnn,
@@ -474,4 +574,4 @@ ALL_PINS = [
     pin_rows_independent,
     pin_initial_state,
     pin_decode_equals_scan,
-]
+] + CONV_PINS

@@ -50,6 +50,20 @@ MUTATIONS = [
      "int64_t i = (t * batch + b) * dim + d;"),
     ("decay_uses_bias_free_delta", "double abar = exp(Delta * A_d[n]);",
      "double abar = exp(softplus(delta_raw) * A_d[n]);"),
+    # causal convolution front-end
+    ("conv_taps_reversed", "v += weight[d * width + j] *", "v += weight[d * width + (width - 1 - j)] *"),
+    ("conv_drop_bias", "double v = bias ? bias[d] : 0.0;\n        for (int64_t j = 0; j < width; ++j)",
+     "double v = 0.0;\n        for (int64_t j = 0; j < width; ++j)"),
+    ("conv_no_silu", "out[(b * seqlen + t) * dim + d] = silu(v);", "out[(b * seqlen + t) * dim + d] = v;"),
+    ("conv_state_out_offset", "conv_input(xin, state_in, seqlen, dim, width, b, d, seqlen - (width - 1) + j);",
+     "conv_input(xin, state_in, seqlen, dim, width, b, d, seqlen - width + j);"),
+    ("conv_state_in_reversed", "return state_in[(b * dim + d) * (width - 1) + (width - 1) + t];",
+     "return state_in[(b * dim + d) * (width - 1) + (-1 - t)];"),
+    ("conv_update_shift_direction", "for (int64_t j = 0; j + 1 < width - 1; ++j) s[j] = s[j + 1];",
+     "for (int64_t j = width - 3; j >= 0; --j) s[j + 1] = s[j];"),
+    ("conv_update_new_input_tap", "v += w[width - 1] * xin[b * dim + d];", "v += w[0] * xin[b * dim + d];"),
+    ("conv_update_drops_bias", "double v = bias ? bias[d] : 0.0;\n      for (int64_t j = 0; j < width - 1; ++j)",
+     "double v = 0.0;\n      for (int64_t j = 0; j < width - 1; ++j)"),
 ]
 
 RUNNER = textwrap.dedent("""
