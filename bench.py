@@ -36,6 +36,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "scan": ["scan_fwd.hip", "device_math.h", "kernels.h"],
     "decode": ["state_update.hip", "device_math.h", "kernels.h"],
+    "conv": ["conv1d.hip", "device_math.h", "conv.h"],
+    "conv_update": ["conv1d.hip", "device_math.h", "conv.h"],
 }
 
 
@@ -93,6 +95,22 @@ def decode_bytes(w) -> int:
     rows = w.batch * w.dim
     return (2 * rows * w.dstate * 4 + rows * eb * 4 + 2 * w.batch * w.dstate * eb
             + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+
+
+def conv_bytes(w, width=4) -> int:
+    """Algorithmic HBM bytes of one conv1d_fwd call: xin read and out written
+    once (io dtype), the state in and out, taps and bias once per channel."""
+    eb = 2 if w.io == "bf16" else 4
+    elems = w.batch * w.seqlen * w.dim
+    return 2 * elems * eb + 2 * w.batch * w.dim * (width - 1) * eb + w.dim * (width + 1) * 4
+
+
+def conv_update_bytes(w, width=4) -> int:
+    """Per decode token: the state read and written, xin read, out written,
+    taps and bias."""
+    eb = 2 if w.io == "bf16" else 4
+    rows = w.batch * w.dim
+    return 2 * rows * (width - 1) * eb + 2 * rows * eb + w.dim * (width + 1) * 4
 
 
 def time_calls(fn, n, stream):
@@ -167,6 +185,7 @@ def main():
     ap.add_argument("--segments", type=int, default=0, help="force time segments (0 = library plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -287,6 +306,53 @@ def main():
                          "algorithmic_bytes_per_launch": db},
         }
         del toks, state
+
+    if not args.no_conv:
+        from selective_state_space_56_amd import conv1d_fwd, conv1d_update
+        from selective_state_space_56_amd.workloads import make_conv_inputs
+        ci = make_conv_inputs(w, 4, device=dev)
+        cout = torch.empty_like(ci["xin"])
+        cst = torch.empty_like(ci["state"])
+
+        def cstep():
+            conv1d_fwd(ci["xin"], ci["weight"], ci["bias"], ci["state"], out=cout, state_out=cst)
+
+        for _ in range(args.warmup):
+            cstep()
+        torch.cuda.synchronize()
+        ccalls = time_calls(cstep, args.steps, stream)
+        cms = sum(ccalls) / len(ccalls)
+        cb = conv_bytes(w)
+        rec["conv"] = {
+            "op": "mamba_conv1d_fwd (causal depthwise conv, width 4, + SiLU)", "workload": w.name,
+            "avg_launch_ms": cms, **call_stats(ccalls),
+            "value": w.elem_steps / (cms * 1e-3), "unit": "elem-steps/s",
+            "roofline": {"bound": "hbm", "achieved": cb / (cms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("conv", w.name),
+                         "algorithmic_bytes_per_launch": cb},
+        }
+        wd = WORKLOADS["decode_4096"]
+        cd = make_conv_inputs(wd.with_shape(seqlen=1), 4, device=dev)
+        cstate = cd["state"].clone()
+        cx = cd["xin"][:, 0].contiguous()
+        cdo = torch.empty_like(cx)
+        for _ in range(4):
+            conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo)
+        torch.cuda.synchronize()
+        ucalls = time_calls(lambda: conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo),
+                            wd.decode_steps, stream)
+        ums = sum(ucalls) / len(ucalls)
+        ub = conv_update_bytes(wd)
+        rec["conv"]["decode"] = {
+            "op": "mamba_conv1d_update", "workload": wd.name, "avg_launch_ms": ums,
+            **call_stats(ucalls),
+            "roofline": {"bound": "hbm", "achieved": ub / (ums * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ub / (ums * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("conv_update", wd.name),
+                         "algorithmic_bytes_per_launch": ub},
+        }
+        del ci, cout, cst, cd, cstate
 
     if not args.no_cpu_baseline:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))

@@ -33,6 +33,11 @@ class Desc(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("width", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -63,6 +68,10 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_state_update.restype = ctypes.c_int
         lib.mamba_state_update.argtypes = [ctypes.POINTER(Desc), fp, vp, vp, fp, vp, vp, fp, vp, fp,
                                            vp, vp]
+        lib.mamba_conv1d_fwd.restype = ctypes.c_int
+        lib.mamba_conv1d_fwd.argtypes = [ctypes.POINTER(ConvDesc), vp, fp, fp, vp, vp, vp, vp]
+        lib.mamba_conv1d_update.restype = ctypes.c_int
+        lib.mamba_conv1d_update.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, fp, fp, vp, vp]
         lib.mamba_status_string.restype = ctypes.c_char_p
         lib.mamba_status_string.argtypes = [ctypes.c_int]
         lib.mamba_last_error.restype = ctypes.c_char_p
@@ -189,5 +198,67 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(dev))
+    _check(lib, st)
+    return out
+
+
+def conv1d_fwd(xin, weight, bias=None, state_in=None, *, out=None, state_out=None,
+               return_state=True):
+    """Causal depthwise convolution + SiLU over full sequences
+    (mamba_conv1d_fwd). xin: (batch, L, dim) float32 or bfloat16 on a GPU;
+    weight: (dim, width) float32; bias: (dim,) float32 or None; state_in:
+    (batch, dim, width - 1) in xin's dtype or None (zeros). Returns
+    (out (batch, L, dim), state_out (batch, dim, width - 1) or None)."""
+    lib = load_library()
+    if xin.dim() != 3 or weight.dim() != 2:
+        raise ValueError("xin must be (batch, L, dim) and weight (dim, width)")
+    batch, L, dim = xin.shape
+    width = weight.shape[1]
+    dev = xin.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_fwd runs on a GPU tensor")
+    io = xin.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(xin, "xin", (batch, L, dim), io, dev)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev)
+    _need(state_in, "state_in", (batch, dim, width - 1), io, dev)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=io, device=dev)
+    _need(out, "out", (batch, L, dim), io, dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((batch, dim, width - 1), dtype=io, device=dev)
+    _need(state_out, "state_out", (batch, dim, width - 1), io, dev)
+    d = ConvDesc(batch, L, dim, width, _IO[io], 0)
+    st = lib.mamba_conv1d_fwd(ctypes.byref(d), _ptr(xin), _ptr(weight), _ptr(bias), _ptr(state_in),
+                              _ptr(out), _ptr(state_out), _stream(dev))
+    _check(lib, st)
+    return out, state_out
+
+
+def conv1d_update(state, xin, weight, bias=None, *, out=None):
+    """One decode token of the convolution (mamba_conv1d_update): advances
+    ``state`` (batch, dim, width - 1) in place and returns out (batch, dim)."""
+    lib = load_library()
+    if xin.dim() != 2 or weight.dim() != 2:
+        raise ValueError("xin must be (batch, dim) and weight (dim, width)")
+    batch, dim = xin.shape
+    width = weight.shape[1]
+    dev = xin.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_update runs on a GPU tensor")
+    io = xin.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(state, "state", (batch, dim, width - 1), io, dev)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    _need(out, "out", (batch, dim), io, dev)
+    d = ConvDesc(batch, 1, dim, width, _IO[io], 0)
+    st = lib.mamba_conv1d_update(ctypes.byref(d), _ptr(state), _ptr(xin), _ptr(weight), _ptr(bias),
+                                 _ptr(out), _stream(dev))
     _check(lib, st)
     return out

@@ -1,14 +1,17 @@
 // C ABI of the selective scan library: argument validation, planning and
 // dispatch to the HIP kernels. See include/mamba_scan.h for the contract.
 #include "mamba_scan.h"
+#include "mamba_conv.h"
 
 #include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
+#include "conv.h"
 #include "kernels.h"
 
 namespace {
@@ -286,6 +289,144 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
   const hipError_t e = mscan::launch_state_update(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+
+}  // extern "C"
+
+namespace {
+
+// Descriptor fields common to both convolution entry points.
+mamba_status check_conv_desc(const mamba_conv_desc* d, const char* who) {
+  if (!d) return fail(MAMBA_ERR_INVALID_ARG, "%s: desc is NULL", who);
+  if (d->batch < 0 || d->seqlen < 0 || d->dim < 0)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: negative size (batch=%lld seqlen=%lld dim=%lld)", who,
+                (long long)d->batch, (long long)d->seqlen, (long long)d->dim);
+  if (d->io_dtype != MAMBA_F32 && d->io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: io_dtype %d is not MAMBA_F32 or MAMBA_BF16", who,
+                (int)d->io_dtype);
+  if (d->width < 1) return fail(MAMBA_ERR_INVALID_ARG, "%s: width %lld < 1", who, (long long)d->width);
+  if (d->width > 4)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: width %lld not supported (1 to 4)", who,
+                (long long)d->width);
+  if (d->flags != 0) return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0", who);
+  const int64_t lim = int64_t(1) << 40;
+  if (d->batch > 65535 || d->seqlen > lim || d->dim > (int64_t(1) << 31) ||
+      (d->batch && d->dim > (int64_t(1) << 31) / d->batch) ||
+      (d->batch * d->dim && d->seqlen > lim / (d->batch * d->dim)) ||
+      (d->seqlen + 63) / 64 > 65535)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: problem too large", who);
+  return MAMBA_OK;
+}
+
+mamba_status check_align(const char* who, std::initializer_list<Span> spans, size_t align) {
+  for (const Span& s : spans)
+    if (s.p && reinterpret_cast<uintptr_t>(s.p) % align)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, align);
+  return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mamba_status mamba_conv1d_fwd(const mamba_conv_desc* d, const void* xin, const float* weight,
+                              const float* bias, const void* state_in, void* out,
+                              void* state_out, void* stream) {
+  const char* who = "mamba_conv1d_fwd";
+  mamba_status st = check_conv_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  const int64_t rows = d->batch * d->dim;
+  const int64_t elems = rows * d->seqlen;
+  if (rows == 0) return ok();
+  if (elems > 0) {
+    if (!xin) return fail(MAMBA_ERR_INVALID_ARG, "%s: xin is NULL", who);
+    if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
+  }
+  if (!weight) return fail(MAMBA_ERR_INVALID_ARG, "%s: weight is NULL", who);
+  const size_t eb = io_bytes(d->io_dtype);
+  const size_t W = static_cast<size_t>(d->width);
+  const size_t state_bytes = static_cast<size_t>(rows) * (W - 1) * eb;
+  const Span in[] = {
+      {"xin", xin, static_cast<size_t>(elems) * eb},
+      {"weight", weight, static_cast<size_t>(d->dim) * W * 4},
+      {"bias", bias, static_cast<size_t>(d->dim) * 4},
+      {"state_in", W > 1 ? state_in : nullptr, state_bytes},
+  };
+  const Span o_out{"out", out, static_cast<size_t>(elems) * eb};
+  const Span o_st{"state_out", W > 1 ? state_out : nullptr, state_bytes};
+  for (const Span& s : in) {
+    if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
+    if (overlaps(o_st, s))
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: state_out overlaps %s", who, s.name);
+  }
+  if (overlaps(o_out, o_st)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps state_out", who);
+  if ((st = check_align(who, {in[0], in[3], o_out, o_st}, eb)) != MAMBA_OK) return st;
+  if ((st = check_align(who, {in[1], in[2]}, 4)) != MAMBA_OK) return st;
+
+  mscan::ConvProblem p{};
+  p.xin = xin;
+  p.weight = weight;
+  p.bias = bias;
+  p.state_in = W > 1 ? state_in : nullptr;
+  p.out = out;
+  p.state_out = W > 1 ? state_out : nullptr;
+  p.batch = d->batch;
+  p.seqlen = d->seqlen;
+  p.dim = d->dim;
+  p.width = static_cast<int>(W);
+  p.io = d->io_dtype;
+  const hipError_t e = mscan::launch_conv1d(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+mamba_status mamba_conv1d_update(const mamba_conv_desc* d, void* state, const void* xin,
+                                 const float* weight, const float* bias, void* out, void* stream) {
+  const char* who = "mamba_conv1d_update";
+  mamba_status st = check_conv_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  if (d->seqlen != 1)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
+  const int64_t rows = d->batch * d->dim;
+  if (rows == 0) return ok();
+  const size_t W = static_cast<size_t>(d->width);
+  if (W > 1 && !state) return fail(MAMBA_ERR_INVALID_ARG, "%s: state is NULL", who);
+  if (!xin) return fail(MAMBA_ERR_INVALID_ARG, "%s: xin is NULL", who);
+  if (!weight) return fail(MAMBA_ERR_INVALID_ARG, "%s: weight is NULL", who);
+  if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
+  const size_t eb = io_bytes(d->io_dtype);
+  const Span in[] = {
+      {"xin", xin, static_cast<size_t>(rows) * eb},
+      {"weight", weight, static_cast<size_t>(d->dim) * W * 4},
+      {"bias", bias, static_cast<size_t>(d->dim) * 4},
+  };
+  const Span o_state{"state", W > 1 ? state : nullptr, static_cast<size_t>(rows) * (W - 1) * eb};
+  const Span o_out{"out", out, static_cast<size_t>(rows) * eb};
+  for (const Span& s : in) {
+    if (overlaps(o_state, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: state overlaps %s", who, s.name);
+    if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
+  }
+  if (overlaps(o_out, o_state)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps state", who);
+  if ((st = check_align(who, {in[0], o_state, o_out}, eb)) != MAMBA_OK) return st;
+  if ((st = check_align(who, {in[1], in[2]}, 4)) != MAMBA_OK) return st;
+
+  mscan::ConvProblem p{};
+  p.xin = xin;
+  p.weight = weight;
+  p.bias = bias;
+  p.out = out;
+  p.state = W > 1 ? state : nullptr;
+  p.batch = d->batch;
+  p.seqlen = 1;
+  p.dim = d->dim;
+  p.width = static_cast<int>(W);
+  p.io = d->io_dtype;
+  const hipError_t e = mscan::launch_conv1d_update(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

@@ -117,6 +117,29 @@ def make_trained_A(w: Workload, device="cpu", seed=0, spread=0.5, channels=None)
     return A.contiguous()
 
 
+def make_conv_params(w: Workload, width=4, device="cpu", seed=0):
+    """Depthwise convolution taps (dim, width) and bias (dim,), fp32, drawn
+    uniform in [-1/sqrt(width), 1/sqrt(width)] (the usual initialisation of a
+    convolution whose fan-in is its width), from their own generator."""
+    g = _gen(device, seed + 271828)
+    k = 1.0 / math.sqrt(width)
+    weight = (torch.rand((w.dim, width), generator=g, device=device) * 2 - 1) * k
+    bias = (torch.rand(w.dim, generator=g, device=device) * 2 - 1) * k
+    return {"weight": weight.contiguous(), "bias": bias}
+
+
+def make_conv_inputs(w: Workload, width=4, device="cpu", seed=0):
+    """The convolution's input xin ~ N(0, 1) (batch, L, dim) and a state
+    (batch, dim, width - 1) ~ N(0, 1) holding earlier inputs, in the io
+    dtype, plus make_conv_params()."""
+    g = _gen(device, seed + 161803)
+    xin = torch.randn((w.batch, w.seqlen, w.dim), generator=g, device=device)
+    state = torch.randn((w.batch, w.dim, width - 1), generator=g, device=device)
+    out = {"xin": xin.to(w.torch_io), "state": state.to(w.torch_io)}
+    out.update(make_conv_params(w, width, device, seed))
+    return out
+
+
 def make_scan_inputs(w: Workload, device="cpu", seed=0):
     """x, delta (Delta_raw), z: (batch, L, dim); B, C: (batch, L, N) in the
     workload's io dtype; plus make_params(). z is None without a gate."""

@@ -10,16 +10,19 @@ import pytest
 from selective_state_space_56_amd import binding as bd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 INVALID, UNSUPPORTED = 1, 2
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +36,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_init",
-                          "mamba_state_update", "mamba_status_string", "mamba_last_error"}
+                          "mamba_state_update", "mamba_status_string", "mamba_last_error",
+                          "mamba_conv1d_fwd", "mamba_conv1d_update"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -184,3 +188,55 @@ def test_state_update_validation(lib):
     assert "16-byte" in err(lib)
     assert upd(lib, D_(batch=0, seqlen=1), state=None, x=None, delta=None, A=None, B=None,
                C=None, out=None) == 0
+
+
+def CD(batch=2, seqlen=8, dim=16, width=4, io=1, flags=0):
+    return bd.ConvDesc(batch, seqlen, dim, width, io, flags)
+
+
+def conv(lib, desc, xin=1, weight=2, bias=3, sin=4, out=5, sout=6):
+    args = [xin, weight, bias, sin, out, sout]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    return lib.mamba_conv1d_fwd(None if desc is None else ctypes.byref(desc), *ptrs, None)
+
+
+def conv_upd(lib, desc, state=4, xin=1, weight=2, bias=3, out=5):
+    args = [state, xin, weight, bias, out]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    return lib.mamba_conv1d_update(None if desc is None else ctypes.byref(desc), *ptrs, None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, None) == INVALID
+    assert conv(lib, CD(width=0)) == INVALID
+    assert conv(lib, CD(width=5)) == UNSUPPORTED
+    assert "width" in err(lib)
+    assert conv(lib, CD(io=3)) == INVALID
+    assert conv(lib, CD(flags=1)) == INVALID
+    assert conv(lib, CD(batch=-1)) == INVALID
+    for missing in ("xin", "weight", "out"):
+        kw = {missing: None}
+        assert conv(lib, CD(), **kw) == INVALID, missing
+        assert missing in err(lib)
+    assert conv(lib, CD(), out=1) == INVALID                 # out == xin
+    assert "out overlaps xin" in err(lib)
+    assert conv(lib, CD(), sout=4) == INVALID                # state_out == state_in
+    assert "state_out overlaps state_in" in err(lib)
+    assert conv(lib, CD(), sout=5) == INVALID                # state_out == out
+    assert conv(lib, CD(), out=ctypes.c_void_p(FAKE + 0x100000 * 5 + 1)) == INVALID
+    assert "aligned" in err(lib)
+    assert conv(lib, CD(), weight=ctypes.c_void_p(FAKE + 0x100000 * 2 + 2)) == INVALID
+    # nothing to do: no rows
+    assert conv(lib, CD(batch=0), xin=None, weight=None, out=None) == 0
+
+
+def test_conv_update_validation(lib):
+    assert conv_upd(lib, CD(seqlen=2)) == INVALID
+    assert "seqlen must be 1" in err(lib)
+    assert conv_upd(lib, CD(seqlen=1, width=7)) == UNSUPPORTED
+    for missing in ("state", "xin", "weight", "out"):
+        assert conv_upd(lib, CD(seqlen=1), **{missing: None}) == INVALID, missing
+        assert missing in err(lib)
+    assert conv_upd(lib, CD(seqlen=1), out=4) == INVALID     # out == state
+    assert conv_upd(lib, CD(seqlen=1), state=1) == INVALID   # state == xin
+    assert "state overlaps xin" in err(lib)
