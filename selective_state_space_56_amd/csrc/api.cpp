@@ -234,6 +234,8 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   if (d->flags != 0) return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0", who);
   if (d->seqlen != 1)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
+  if ((d->batch + 15) / 16 > 65535)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: batch %lld too large", who, (long long)d->batch);
   const int64_t rows = d->batch * d->dim;
   if (rows == 0) return ok();
   if (!state) return fail(MAMBA_ERR_INVALID_ARG, "%s: state is NULL", who);

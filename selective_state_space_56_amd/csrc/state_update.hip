@@ -11,9 +11,11 @@
 // The kernel is a single streaming pass over the state: each row's N states
 // are split over N / 4 lanes that hold four consecutive states each, so one
 // wave64 reads and writes a contiguous run of 64 x 16 bytes with 16-byte
-// vector accesses. The per-row front-end (softplus, gate) is recomputed by
-// each lane of the row; the C read-out is summed across the row's lanes with
-// cross-lane shuffles.
+// vector accesses. A thread keeps its channel's parameters (four states' A,
+// D, bias) in registers and serves kDecodeRows batch rows in turn, so the
+// per-channel parameters are read once per run of rows, not once per row. The
+// per-row front-end (softplus, gate) is recomputed by each lane of the row;
+// the C read-out is summed across the row's lanes with cross-lane shuffles.
 #include "device_math.h"
 #include "kernels.h"
 
@@ -22,6 +24,8 @@ namespace mscan {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kDecodeRows = 16;  // batch rows per thread
+constexpr int kGroupRows = 4;    // rows whose loads are in flight together
 
 struct DecodeKernelArgs {
   float* state;
@@ -34,64 +38,95 @@ struct DecodeKernelArgs {
   const void* z;
   const float* bias;
   void* out;
-  int64_t rows;  // batch * dim
+  int64_t batch;
   int64_t dim;
 };
 
+// Grid: x = (channel, lane-of-row) pairs, kBlock per workgroup; y = runs of
+// kDecodeRows batch rows.
 template <int N, class IO>
 __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a) {
   using raw = typename IO::raw;
   constexpr int SPL = N >= 4 ? 4 : N;  // states per lane
   constexpr int LPR = N / SPL;         // lanes per row (1, 2 or 4; a power of 2)
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t row_raw = gid / LPR;
+  const int64_t d_raw = gid / LPR;
   const int sub = static_cast<int>(gid % LPR);
-  const bool active = row_raw < a.rows;
-  // Inactive lanes of the last block mirror the last row so that the
+  const bool active = d_raw < a.dim;
+  // Inactive lanes of the last workgroup mirror the last channel so that the
   // cross-lane sum below sees full lane groups; they store nothing.
-  const int64_t row = active ? row_raw : a.rows - 1;
-  const int64_t b = row / a.dim;
-  const int64_t d = row - b * a.dim;
+  const int64_t d = active ? d_raw : a.dim - 1;
 
-  const float xf = IO::load(static_cast<const raw*>(a.x) + row);
-  const float bias = a.bias ? a.bias[d] : 0.0f;
-  const float Delta = softplus_f(IO::load(static_cast<const raw*>(a.delta) + row) + bias);
-  const float dx = Delta * xf;
-
-  float* hp = a.state + row * N + sub * SPL;
-  float h[SPL];
-  if constexpr (SPL == 4) {
-    const float4 v = *reinterpret_cast<const float4*>(hp);
-    h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < SPL; ++k) h[k] = hp[k];
-  }
-
-  const raw* Bt = static_cast<const raw*>(a.B) + b * N + sub * SPL;
-  const raw* Ct = static_cast<const raw*>(a.C) + b * N + sub * SPL;
+  float A2[SPL];
   const float* Ad = a.A + d * N + sub * SPL;
-  float y = 0.0f;
 #pragma unroll
-  for (int k = 0; k < SPL; ++k) {
-    const float abar = hw_exp2(Delta * (Ad[k] * kLog2e));
-    h[k] = fmaf(abar, h[k], dx * IO::load(Bt + k));
-    y = fmaf(IO::load(Ct + k), h[k], y);
-  }
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) y += __shfl_xor(y, off);
+  for (int k = 0; k < SPL; ++k) A2[k] = Ad[k] * kLog2e;
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float Dd = a.D ? a.D[d] : 0.0f;
 
-  if (active) {
-    if constexpr (SPL == 4) {
-      *reinterpret_cast<float4*>(hp) = make_float4(h[0], h[1], h[2], h[3]);
-    } else {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kDecodeRows;
+  const int64_t b1 = b0 + kDecodeRows < a.batch ? b0 + kDecodeRows : a.batch;
+  const raw* xp = static_cast<const raw*>(a.x);
+  const raw* dp = static_cast<const raw*>(a.delta);
+  const raw* zp = static_cast<const raw*>(a.z);
+  // Rows are taken kGroupRows at a time: all of a group's loads are issued
+  // before its rows are computed and stored (rows past the batch repeat the
+  // last row and store nothing).
+  for (int64_t g0 = b0; g0 < b1; g0 += kGroupRows) {
+    float xf[kGroupRows], draw[kGroupRows], zf[kGroupRows], h[kGroupRows][SPL];
+    float Bv[kGroupRows][SPL], Cv[kGroupRows][SPL];
 #pragma unroll
-      for (int k = 0; k < SPL; ++k) hp[k] = h[k];
+    for (int r = 0; r < kGroupRows; ++r) {
+      const int64_t b = g0 + r < b1 ? g0 + r : b1 - 1;
+      const int64_t row = b * a.dim + d;
+      xf[r] = IO::load(xp + row);
+      draw[r] = IO::load(dp + row);
+      zf[r] = a.z ? IO::load(zp + row) : 0.0f;
+      const float* hp = a.state + row * N + sub * SPL;
+      if constexpr (SPL == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(hp);
+        h[r][0] = v.x; h[r][1] = v.y; h[r][2] = v.z; h[r][3] = v.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) h[r][k] = hp[k];
+      }
+      const raw* Bt = static_cast<const raw*>(a.B) + b * N + sub * SPL;
+      const raw* Ct = static_cast<const raw*>(a.C) + b * N + sub * SPL;
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) {
+        Bv[r][k] = IO::load(Bt + k);
+        Cv[r][k] = IO::load(Ct + k);
+      }
     }
-    if (sub == 0) {
-      if (a.D) y = fmaf(a.D[d], xf, y);
-      if (a.z) y *= silu_f(IO::load(static_cast<const raw*>(a.z) + row));
-      static_cast<raw*>(a.out)[row] = IO::from_f32(y);
+#pragma unroll
+    for (int r = 0; r < kGroupRows; ++r) {
+      const int64_t b = g0 + r;
+      const float Delta = softplus_f(draw[r] + bias);
+      const float dx = Delta * xf[r];
+      float y = 0.0f;
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) {
+        const float abar = hw_exp2(Delta * A2[k]);
+        h[r][k] = fmaf(abar, h[r][k], dx * Bv[r][k]);
+        y = fmaf(Cv[r][k], h[r][k], y);
+      }
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) y += __shfl_xor(y, off);
+      if (active && b < b1) {
+        const int64_t row = b * a.dim + d;
+        float* hp = a.state + row * N + sub * SPL;
+        if constexpr (SPL == 4) {
+          *reinterpret_cast<float4*>(hp) = make_float4(h[r][0], h[r][1], h[r][2], h[r][3]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < SPL; ++k) hp[k] = h[r][k];
+        }
+        if (sub == 0) {
+          if (a.D) y = fmaf(Dd, xf[r], y);
+          if (a.z) y *= silu_f(zf[r]);
+          static_cast<raw*>(a.out)[row] = IO::from_f32(y);
+        }
+      }
     }
   }
 }
@@ -111,10 +146,11 @@ hipError_t launch_typed(const DecodeProblem& p, hipStream_t stream) {
   a.z = p.z;
   a.bias = p.bias;
   a.out = p.out;
-  a.rows = p.batch * p.dim;
+  a.batch = p.batch;
   a.dim = p.dim;
-  const int64_t threads = a.rows * LPR;
-  const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock));
+  const int64_t threads = p.dim * LPR;
+  const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock),
+                  static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));
   hipLaunchKernelGGL((state_update_kernel<N, IO>), grid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
