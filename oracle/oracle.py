@@ -58,6 +58,8 @@ class Oracle:
         lib.oracle_state_update_f64.restype = ctypes.c_int
         lib.oracle_state_update_f64.argtypes = [_i64, _i64, _i64] + [_dp] * 9 + \
             [ctypes.c_int, _dp, ctypes.c_int]
+        lib.oracle_scan_bwd_f64.restype = ctypes.c_int
+        lib.oracle_scan_bwd_f64.argtypes = [_i64] * 4 + [_dp] * 20 + [ctypes.c_int]
         lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         lib.oracle_conv1d_silu_f64.argtypes = [_i64] * 4 + [_dp] * 6 + [ctypes.c_int]
         lib.oracle_conv1d_update_f64.restype = ctypes.c_int
@@ -114,6 +116,38 @@ class Oracle:
             raise ValueError("oracle_state_update_f64 returned %d" % rc)
         return out, st
 
+
+    def scan_bwd(self, x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, h0=None,
+                 dlast=None, nthreads=None):
+        """Gradients of the scan (first-order B-bar) for dLoss/dout and
+        optionally dLoss/dlast_state. Returns a dict with dx, ddelta, dz
+        (batch, L, dim), dA (dim, N), dB, dC (batch, L, N), dD, dbias (dim,)
+        and dh0 (batch, dim, N), all fp64."""
+        x = _f64(x)
+        batch, L, dim = x.shape
+        A = _f64(A)
+        N = A.shape[1]
+        delta = _f64(delta, x.shape)
+        B = _f64(B, (batch, L, N))
+        C = _f64(C, (batch, L, N))
+        D = _f64(D, (dim,))
+        z = _f64(z, x.shape)
+        delta_bias = _f64(delta_bias, (dim,))
+        h0 = _f64(h0, (batch, dim, N))
+        dout = _f64(dout, x.shape)
+        dlast = _f64(dlast, (batch, dim, N))
+        g = {"dx": np.empty(x.shape), "ddelta": np.empty(x.shape), "dA": np.empty((dim, N)),
+             "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N)), "dD": np.empty(dim),
+             "dz": np.empty(x.shape), "dbias": np.empty(dim), "dh0": np.empty((batch, dim, N))}
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_scan_bwd_f64(
+            batch, L, dim, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(dlast), _ptr(g["dx"]), _ptr(g["ddelta"]),
+            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+            _ptr(g["dbias"]), _ptr(g["dh0"]), nt)
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_f64 returned %d" % rc)
+        return g
 
     def conv1d(self, xin, weight, bias=None, state_in=None, nthreads=None):
         """Causal depthwise convolution + SiLU. xin: (batch, L, dim); weight:

@@ -52,6 +52,9 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* softplus(u) = log(1 + exp(u)), written so that neither branch overflows. */
 static double softplus(double u) {
@@ -235,5 +238,124 @@ int oracle_conv1d_update_f64(int64_t batch, int64_t dim, int64_t width, double *
       if (width > 1) s[width - 2] = xin[b * dim + d];
     }
   }
+  return 0;
+}
+
+/*
+ * Gradients of the scan (first-order B-bar) by the plain reverse pass: the
+ * backward pass of the method ("Mamba and selective state spaces, from first
+ * principles", section "The hardware-aware scan": the backward pass recomputes
+ * the intermediate states instead of storing them; here, on the CPU, every
+ * state of a row is simply kept).
+ *
+ * Given dout = dLoss/dout (batch, seqlen, dim) and optionally
+ * dlast = dLoss/dlast_state (batch, dim, dstate), with
+ *   s_t = sum_n C[t,n] h[t,n] + D x_t,  y_t = s_t * silu(z_t)  (s_t without z),
+ * the adjoint of the state, lambda_t = dLoss/dh_t, obeys
+ *   lambda_{L-1} = ds_{L-1} C_{L-1} + dlast,
+ *   lambda_t     = ds_t C_t + abar_{t+1} lambda_{t+1},     ds_t = dout_t silu(z_t),
+ * and, from h_t = abar_t h_{t-1} + Delta_t x_t B_t with abar_t = exp(Delta_t A):
+ *   dDelta_t = sum_n lambda_t,n (A_n abar_t,n h_{t-1,n} + x_t B_t,n)
+ *   dx_t     = D ds_t + sum_n lambda_t,n Delta_t B_t,n
+ *   dB_t,n  += lambda_t,n Delta_t x_t          (summed over channels)
+ *   dC_t,n  += ds_t h_t,n                       (summed over channels)
+ *   dA_n    += lambda_t,n Delta_t abar_t,n h_{t-1,n}  (summed over batch, time)
+ *   dz_t     = dout_t s_t silu'(z_t)
+ *   ddelta_t = dDelta_t sigmoid(delta_t + bias)  (softplus' = sigmoid)
+ *   dbias   += ddelta_t; dD += ds_t x_t;  dh0 = abar_0 lambda_0.
+ * Outputs: dx, ddelta, dz (batch, seqlen, dim); dA (dim, dstate); dB, dC
+ * (batch, seqlen, dstate); dD, dbias (dim); dh0 (batch, dim, dstate). dz, dD,
+ * dbias, dh0 may be NULL (not wanted); all outputs are overwritten.
+ * Parallel over channels; dB and dC are accumulated per thread, then summed.
+ */
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                        const double *x, const double *delta, const double *A,
+                        const double *B, const double *C, const double *D,
+                        const double *z, const double *delta_bias, const double *h0,
+                        const double *dout, const double *dlast, double *dx,
+                        double *ddelta, double *dA, double *dB, double *dC, double *dD,
+                        double *dz, double *dbias, double *dh0, int nthreads) {
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 64) return -1;
+  if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dA || !dB || !dC)
+    return -1;
+  if (nthreads < 1) nthreads = 1;
+  const int64_t N = dstate, L = seqlen;
+  const int64_t bcn = batch * L * N;
+  double *part = (double *)calloc((size_t)(nthreads * 2 * bcn + 1), sizeof(double));
+  double *hist = (double *)malloc((size_t)(nthreads * (L + 1) * N + 1) * sizeof(double));
+  if (!part || !hist) {
+    free(part);
+    free(hist);
+    return -3;
+  }
+
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int64_t d = 0; d < dim; ++d) {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double *pB = part + (int64_t)tid * 2 * bcn, *pC = pB + bcn;
+    double *hs = hist + (int64_t)tid * (L + 1) * N; /* hs[(t+1)*N + n] = h_t, hs[n] = h_{-1} */
+    const double *A_d = A + d * N;
+    const double bias = delta_bias ? delta_bias[d] : 0.0;
+    double dA_acc[64] = {0}, dD_acc = 0.0, dbias_acc = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t i = (b * L + t) * dim + d, j = (b * L + t) * N;
+        const double Dl = softplus(delta[i] + bias);
+        for (int64_t n = 0; n < N; ++n)
+          hs[(t + 1) * N + n] = exp(Dl * A_d[n]) * hs[t * N + n] + Dl * B[j + n] * x[i];
+      }
+      double lam[64];
+      for (int64_t n = 0; n < N; ++n) lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t i = (b * L + t) * dim + d, j = (b * L + t) * N;
+        const double u = delta[i] + bias, Dl = softplus(u), xt = x[i];
+        double s = D ? D[d] * xt : 0.0;
+        for (int64_t n = 0; n < N; ++n) s += C[j + n] * hs[(t + 1) * N + n];
+        const double g = z ? silu(z[i]) : 1.0;
+        const double ds = dout[i] * g;
+        if (dz) {
+          const double sg = sigmoid(z[i]);
+          dz[i] = z ? dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg)) : 0.0;
+        }
+        double dDl = 0.0, dxt = D ? D[d] * ds : 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          lam[n] += ds * C[j + n];
+          const double abar = exp(Dl * A_d[n]), hprev = hs[t * N + n];
+          pC[j + n] += ds * hs[(t + 1) * N + n];
+          pB[j + n] += lam[n] * Dl * xt;
+          dDl += lam[n] * (A_d[n] * abar * hprev + xt * B[j + n]);
+          dxt += lam[n] * Dl * B[j + n];
+          dA_acc[n] += lam[n] * Dl * abar * hprev;
+          lam[n] *= abar;
+        }
+        dx[i] = dxt;
+        ddelta[i] = dDl * sigmoid(u);
+        dbias_acc += ddelta[i];
+        dD_acc += ds * xt;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * dim + d) * N + n] = lam[n];
+    }
+    for (int64_t n = 0; n < N; ++n) dA[d * N + n] = dA_acc[n];
+    if (dD) dD[d] = dD_acc;
+    if (dbias) dbias[d] = dbias_acc;
+  }
+  for (int64_t k = 0; k < bcn; ++k) {
+    double sb = 0.0, sc = 0.0;
+    for (int th = 0; th < nthreads; ++th) {
+      sb += part[(int64_t)th * 2 * bcn + k];
+      sc += part[(int64_t)th * 2 * bcn + bcn + k];
+    }
+    dB[k] = sb;
+    dC[k] = sc;
+  }
+  free(part);
+  free(hist);
   return 0;
 }

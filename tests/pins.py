@@ -460,6 +460,77 @@ def pin_decode_equals_scan(orc):
 
 
 # ---------------------------------------------------------------------------
+# Gradients (the backward pass)
+# ---------------------------------------------------------------------------
+
+def _bwd_problem(seed, batch=2, L=7, dim=3, N=4):
+    rng = np.random.default_rng(seed)
+    p = dict(x=rng.normal(size=(batch, L, dim)), delta=rng.normal(size=(batch, L, dim)),
+             A=-rng.uniform(0.2, 2, (dim, N)), B=rng.normal(size=(batch, L, N)),
+             C=rng.normal(size=(batch, L, N)), D=rng.normal(size=dim), z=rng.normal(size=(batch, L, dim)),
+             delta_bias=rng.normal(0, .5, dim), h0=rng.normal(size=(batch, dim, N)))
+    dout = rng.normal(size=(batch, L, dim))
+    dlast = rng.normal(size=(batch, dim, N))
+    return p, dout, dlast, rng
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient agrees with central differences of the forward oracle:
+    d/dtheta of sum(dout * y) + sum(dlast * last_state)."""
+    p, dout, dlast, rng = _bwd_problem(41)
+
+    def loss(**kw):
+        a = dict(p)
+        a.update(kw)
+        y, last = orc.scan(a["x"], a["delta"], a["A"], a["B"], a["C"], D=a["D"], z=a["z"],
+                           delta_bias=a["delta_bias"], h0=a["h0"])
+        return float((y * dout).sum() + (last * dlast).sum())
+
+    g = orc.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dout, D=p["D"], z=p["z"],
+                     delta_bias=p["delta_bias"], h0=p["h0"], dlast=dlast)
+    eps = 1e-6
+    for name, gk in [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
+                     ("D", "dD"), ("z", "dz"), ("delta_bias", "dbias"), ("h0", "dh0")]:
+        arr = p[name]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            hi, lo = arr.copy(), arr.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            fd = (loss(**{name: hi}) - loss(**{name: lo})) / (2 * eps)
+            _close(g[gk][idx], fd, 1e-5, 1e-7, f"d{name}{idx}")
+
+
+def pin_bwd_readout_only(orc):
+    """With C = 0 and no final-state gradient nothing flows into the state:
+    dA = dB = ddelta = dh0 = 0, dx = D ds, dD = sum ds x, dbias = 0, and
+    dC = sum_d ds h (the states themselves, from the forward)."""
+    p, dout, _, _ = _bwd_problem(42)
+    C = np.zeros_like(p["C"])
+    g = orc.scan_bwd(p["x"], p["delta"], p["A"], p["B"], C, dout, D=p["D"], z=p["z"],
+                     delta_bias=p["delta_bias"], h0=p["h0"])
+    ds = dout * _silu(p["z"])
+    for k in ("dA", "dB", "ddelta", "dh0", "dbias"):
+        _close(g[k], np.zeros_like(g[k]), 0, 0, k)
+    _close(g["dx"], p["D"] * ds, 1e-14, 1e-15, "dx = D ds")
+    _close(g["dD"], (ds * p["x"]).sum(axis=(0, 1)), 1e-13, 1e-14, "dD")
+    # the states: scan with C = e_n reads state n out as y (no D, no gate)
+    batch, L, dim = p["x"].shape
+    N = p["A"].shape[1]
+    want = np.zeros((batch, L, N))
+    for n in range(N):
+        e = np.zeros((batch, L, N))
+        e[:, :, n] = 1.0
+        h_n, _ = orc.scan(p["x"], p["delta"], p["A"], p["B"], e, delta_bias=p["delta_bias"],
+                          h0=p["h0"])
+        want[:, :, n] = (ds * h_n).sum(axis=2)
+    _close(g["dC"], want, 1e-12, 1e-13, "dC")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_readout_only]
+
+
+# ---------------------------------------------------------------------------
 # Causal depthwise convolution + SiLU (the SSM branch's front-end:
 # ai.thesatyajit.com, "The Mamba block"; erikxu.me notes, "Mamba")
 # ---------------------------------------------------------------------------
@@ -574,4 +645,4 @@ ALL_PINS = [
     pin_rows_independent,
     pin_initial_state,
     pin_decode_equals_scan,
-] + CONV_PINS
+] + CONV_PINS + BWD_PINS

@@ -50,6 +50,18 @@ MUTATIONS = [
      "int64_t i = (t * batch + b) * dim + d;"),
     ("decay_uses_bias_free_delta", "double abar = exp(Delta * A_d[n]);",
      "double abar = exp(softplus(delta_raw) * A_d[n]);"),
+    # backward pass
+    ("bwd_no_adjoint_decay", "          lam[n] *= abar;\n", ""),
+    ("bwd_dC_previous_state", "pC[j + n] += ds * hs[(t + 1) * N + n];", "pC[j + n] += ds * hs[t * N + n];"),
+    ("bwd_dB_without_delta", "pB[j + n] += lam[n] * Dl * xt;", "pB[j + n] += lam[n] * xt;"),
+    ("bwd_dA_without_abar", "dA_acc[n] += lam[n] * Dl * abar * hprev;", "dA_acc[n] += lam[n] * Dl * hprev;"),
+    ("bwd_dx_without_D", "double dDl = 0.0, dxt = D ? D[d] * ds : 0.0;", "double dDl = 0.0, dxt = 0.0;"),
+    ("bwd_softplus_grad_sign", "ddelta[i] = dDl * sigmoid(u);", "ddelta[i] = dDl * sigmoid(-u);"),
+    ("bwd_dz_silu_grad", "dz[i] = z ? dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg)) : 0.0;",
+     "dz[i] = z ? dout[i] * s * sg : 0.0;"),
+    ("bwd_dlast_dropped", "lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+    ("bwd_ddelta_misses_input_term", "dDl += lam[n] * (A_d[n] * abar * hprev + xt * B[j + n]);",
+     "dDl += lam[n] * (A_d[n] * abar * hprev);"),
     # causal convolution front-end
     ("conv_taps_reversed", "v += weight[d * width + j] *", "v += weight[d * width + (width - 1 - j)] *"),
     ("conv_drop_bias", "double v = bias ? bias[d] : 0.0;\n        for (int64_t j = 0; j < width; ++j)",
