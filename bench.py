@@ -34,7 +34,7 @@ ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PUBLISHED_FP32_VECTOR_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "scan": ["scan_fwd.hip", "device_math.h", "kernels.h"],
+    "scan": ["scan_fwd.hip", "tile_io.h", "device_math.h", "kernels.h"],
     "decode": ["state_update.hip", "device_math.h", "kernels.h"],
     "conv": ["conv1d.hip", "device_math.h", "conv.h"],
     "conv_update": ["conv1d.hip", "device_math.h", "conv.h"],

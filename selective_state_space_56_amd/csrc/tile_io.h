@@ -1,0 +1,189 @@
+// Channel-tile staging shared by the full-sequence scan kernels (forward and
+// backward) on gfx950: tile geometry, global-to-LDS copies of input tiles
+// through buffer resources, tile stores, and the B/C tile of a chunk.
+#pragma once
+
+#include "device_math.h"
+
+namespace mscan {
+
+
+#ifndef MSCAN_BLOCK
+#define MSCAN_BLOCK 256
+#endif
+constexpr int kBlock = MSCAN_BLOCK;  // lanes (channels) per scan workgroup, a multiple of 64
+static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
+constexpr int kAuxBlock = 256;       // threads per workgroup of the small helper kernels
+constexpr int kChunk = 8;     // time steps whose inputs are loaded together
+
+// p[n] = rho e^(n+1) for n = 0..N-1: rho e, then blocks doubling in length,
+// block b (n = b .. 2b-1) being block 0 .. b-1 times e^b (N + log2 N - 1
+// multiplications, at most 1 + log2 N deep).
+template <int N>
+__device__ __forceinline__ void scaled_powers(float e, float rho, float (&p)[N]) {
+  p[0] = rho * e;
+  float eb = e;
+#pragma unroll
+  for (int b = 1; b < N; b *= 2) {
+    if (b > 1) eb = eb * eb;
+#pragma unroll
+    for (int i = 0; i < b; ++i) p[b + i] = p[i] * eb;
+  }
+}
+
+using lds_void = __attribute__((address_space(3))) void;
+
+// Per-lane byte offset of a tile piece: a tile of kChunk rows (steps) by
+// kBlock channels is moved S bytes per lane, lane i of instruction k taking
+// the piece (k * kBlock + i) * S bytes into the tile; each instruction covers
+// S / eb whole rows, so the offset within the instruction's rows is the same
+// for every k. Pieces past the last channel get kOffNone.
+template <class IO, int S>
+__device__ __forceinline__ uint32_t tile_lane_offset(uint32_t row_bytes, uint32_t valid_bytes) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const uint32_t flat = threadIdx.x * S;
+  const uint32_t row = flat / (kBlock * eb), col = flat % (kBlock * eb);
+  return col + S <= valid_bytes ? row * row_bytes + col : kOffNone;
+}
+
+// Copy rows 0 .. kChunk - 1 (from `rows`, the tile's first element in the
+// chunk's first step) of one input tensor's channel tile straight from global
+// memory into LDS (buffer_load ... lds: no registers involved). Each copy
+// instruction gets its own buffer resource, built in scalar registers, that
+// starts at its first row and ends at the segment's end (`rows_left` rows from
+// `rows`): rows past the segment read as zero, as do pieces past the last
+// channel (`lane_off`); they are never used. Lane i of wave `wv` lands S * i
+// bytes after the wave's LDS base.
+template <class IO, int S>
+__device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t rows_left,
+                                         uint32_t row_bytes, typename IO::raw* tile, int wv,
+                                         uint32_t lane_off) {
+  constexpr int eb = sizeof(typename IO::raw);
+  constexpr int kTileBytes = kChunk * kBlock * eb;
+  constexpr int kPerInstr = kBlock * S;
+  constexpr int kRowsPerInstr = S / eb;
+  static_assert(kTileBytes % kPerInstr == 0, "tile must be a whole number of copies");
+  static_assert(S == 16 || S == 4, "copies are 16 or 4 bytes per lane");
+#pragma unroll
+  for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
+    const uint32_t r0 = k * kRowsPerInstr;
+    const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+    const auto r = make_rsrc(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
+    char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + wv * 64) * S;
+    if constexpr (S == 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, lane_off, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, lane_off, 0, 0, 0);
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Write the y tile of one chunk from LDS to HBM in the pieces of dma_tile
+// (same per-instruction resources, so rows past the segment are dropped), or,
+// with S == 0, each lane its own channel (`ch_off`, kOffNone past the last
+// channel) row by row.
+template <class IO, int S>
+__device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows_left,
+                                           uint32_t row_bytes, const typename IO::raw* tile,
+                                           uint32_t lane_off, uint32_t ch_off) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const int tid = threadIdx.x;
+  if constexpr (S == 0) {
+    const auto r = make_rsrc(rows);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+      if (static_cast<uint32_t>(j) < rows_left)
+        IO::bstore(tile[j * kBlock + tid], r, ch_off, j * row_bytes);
+  } else {
+    constexpr int kTileBytes = kChunk * kBlock * eb;
+    constexpr int kPerInstr = kBlock * S;
+    constexpr int kRowsPerInstr = S / eb;
+#pragma unroll
+    for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
+      const uint32_t r0 = k * kRowsPerInstr;
+      const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+      const auto r = make_rsrc(reinterpret_cast<char*>(rows) + r0 * row_bytes, left * row_bytes);
+      const char* src = reinterpret_cast<const char*>(tile) + (k * kBlock + tid) * S;
+      if constexpr (S == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, lane_off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), r, lane_off, 0,
+                                              0);
+    }
+  }
+}
+
+// Register-staged copy for tiles that are not a whole number of 32-bit words
+// (an odd number of bf16 channels): each lane loads its own channel's value
+// for every step of the chunk, and writes them to LDS after the current chunk
+// has been computed.
+template <class IO>
+struct TileRegs {
+  typename IO::raw v[kChunk];
+};
+
+template <class IO>
+__device__ __forceinline__ void load_tile_regs(TileRegs<IO>& tr, const typename IO::raw* rows,
+                                               uint32_t rows_left, uint32_t row_bytes,
+                                               uint32_t ch_off) {
+  const auto r = make_rsrc(rows);
+#pragma unroll
+  for (int j = 0; j < kChunk; ++j)
+    tr.v[j] = IO::bload(r, static_cast<uint32_t>(j) < rows_left ? ch_off : kOffNone, j * row_bytes);
+}
+
+template <class IO>
+__device__ __forceinline__ void store_tile_regs(const TileRegs<IO>& tr, typename IO::raw* tile) {
+#pragma unroll
+  for (int j = 0; j < kChunk; ++j) tile[j * kBlock + threadIdx.x] = tr.v[j];
+}
+
+// Thread i < kChunk * 2N fetches element i of a chunk's B/C tile: B or C of
+// step i / 2N, state i % 2N (C when i % 2N >= N). Its byte offsets into B and
+// into C (kOffNone for the tensor it does not read, and for i past the tile):
+struct BcOffsets {
+  uint32_t b, c;
+};
+template <int N, class IO>
+__device__ __forceinline__ BcOffsets bc_offsets(int i) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const int j = i / (2 * N), k = i % (2 * N);
+  const bool in_tile = i < kChunk * 2 * N;
+  return {in_tile && k < N ? static_cast<uint32_t>((j * N + k) * eb) : kOffNone,
+          in_tile && k >= N ? static_cast<uint32_t>((j * N + k - N) * eb) : kOffNone};
+}
+
+// This thread's B/C tile element for the chunk whose first step is row 0 of
+// Bc / Cc (`rows_left` steps to the segment's end; steps past it read 0 and are
+// never used), widened to fp32.
+template <int N, class IO>
+__device__ __forceinline__ float bc_elem(const typename IO::raw* Bc, const typename IO::raw* Cc,
+                                         uint32_t rows_left, BcOffsets o) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const uint32_t bytes = rows_left * N * eb;
+  const auto rb = make_rsrc(Bc, bytes), rc = make_rsrc(Cc, bytes);
+  return IO::to_f32(IO::bit_or(IO::bload(rb, o.b, 0), IO::bload(rc, o.c, 0)));
+}
+
+template <int N>
+__device__ __forceinline__ void read_bc(const float* row, float (&bc)[2 * N], bool need_c) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < 2 * N; k += 4) {
+      if (k >= N && !need_c) break;
+      const float4 q = *reinterpret_cast<const float4*>(row + k);
+      bc[k] = q.x;
+      bc[k + 1] = q.y;
+      bc[k + 2] = q.z;
+      bc[k + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2 * N; ++k) bc[k] = (k < N || need_c) ? row[k] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace mscan
