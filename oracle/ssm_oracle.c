@@ -320,8 +320,12 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
         const double g = z ? silu(z[i]) : 1.0;
         const double ds = dout[i] * g;
         if (dz) {
-          const double sg = sigmoid(z[i]);
-          dz[i] = z ? dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg)) : 0.0;
+          if (z) {
+            const double sg = sigmoid(z[i]);
+            dz[i] = dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg));
+          } else {
+            dz[i] = 0.0; /* no gate: y does not depend on z */
+          }
         }
         double dDl = 0.0, dxt = D ? D[d] * ds : 0.0;
         for (int64_t n = 0; n < N; ++n) {

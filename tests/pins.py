@@ -477,21 +477,41 @@ def _bwd_problem(seed, batch=2, L=7, dim=3, N=4):
 def pin_bwd_finite_differences(orc):
     """Every gradient agrees with central differences of the forward oracle:
     d/dtheta of sum(dout * y) + sum(dlast * last_state)."""
-    p, dout, dlast, rng = _bwd_problem(41)
+    _bwd_fd_check(orc, 41, gated=True)
+
+
+def pin_bwd_finite_differences_bare(orc):
+    """The same without gate, D, bias, initial state or final-state gradient;
+    then also dz = 0, dD = sum dout x and dbias = sum ddelta."""
+    _bwd_fd_check(orc, 43, gated=False)
+
+
+def _bwd_fd_check(orc, seed, gated):
+    p, dout, dlast, rng = _bwd_problem(seed)
+    if not gated:
+        for k in ("D", "z", "delta_bias", "h0"):
+            p[k] = None
+        dlast = None
 
     def loss(**kw):
         a = dict(p)
         a.update(kw)
         y, last = orc.scan(a["x"], a["delta"], a["A"], a["B"], a["C"], D=a["D"], z=a["z"],
                            delta_bias=a["delta_bias"], h0=a["h0"])
-        return float((y * dout).sum() + (last * dlast).sum())
+        return float((y * dout).sum() + (0.0 if dlast is None else (last * dlast).sum()))
 
     g = orc.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], dout, D=p["D"], z=p["z"],
                      delta_bias=p["delta_bias"], h0=p["h0"], dlast=dlast)
+    if not gated:
+        _close(g["dz"], np.zeros_like(g["dz"]), 0, 0, "dz without a gate")
+        _close(g["dD"], (dout * p["x"]).sum(axis=(0, 1)), 1e-13, 1e-14, "dD without a gate")
+        _close(g["dbias"], g["ddelta"].sum(axis=(0, 1)), 1e-12, 1e-14, "dbias = sum ddelta")
     eps = 1e-6
     for name, gk in [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
                      ("D", "dD"), ("z", "dz"), ("delta_bias", "dbias"), ("h0", "dh0")]:
         arr = p[name]
+        if arr is None:
+            continue
         for _ in range(6):
             idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
             hi, lo = arr.copy(), arr.copy()
@@ -527,7 +547,7 @@ def pin_bwd_readout_only(orc):
     _close(g["dC"], want, 1e-12, 1e-13, "dC")
 
 
-BWD_PINS = [pin_bwd_finite_differences, pin_bwd_readout_only]
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_bare, pin_bwd_readout_only]
 
 
 # ---------------------------------------------------------------------------

@@ -57,8 +57,8 @@ MUTATIONS = [
     ("bwd_dA_without_abar", "dA_acc[n] += lam[n] * Dl * abar * hprev;", "dA_acc[n] += lam[n] * Dl * hprev;"),
     ("bwd_dx_without_D", "double dDl = 0.0, dxt = D ? D[d] * ds : 0.0;", "double dDl = 0.0, dxt = 0.0;"),
     ("bwd_softplus_grad_sign", "ddelta[i] = dDl * sigmoid(u);", "ddelta[i] = dDl * sigmoid(-u);"),
-    ("bwd_dz_silu_grad", "dz[i] = z ? dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg)) : 0.0;",
-     "dz[i] = z ? dout[i] * s * sg : 0.0;"),
+    ("bwd_dz_silu_grad", "dz[i] = dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg));",
+     "dz[i] = dout[i] * s * sg;"),
     ("bwd_dlast_dropped", "lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
     ("bwd_ddelta_misses_input_term", "dDl += lam[n] * (A_d[n] * abar * hprev + xt * B[j + n]);",
      "dDl += lam[n] * (A_d[n] * abar * hprev);"),
