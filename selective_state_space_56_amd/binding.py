@@ -65,6 +65,11 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_scan_fwd_init.restype = ctypes.c_int
         lib.mamba_scan_fwd_init.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, fp,
                                             vp, fp, vp, sz, vp]
+        lib.mamba_scan_bwd_workspace_size.restype = sz
+        lib.mamba_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        lib.mamba_scan_bwd.restype = ctypes.c_int
+        lib.mamba_scan_bwd.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, fp,
+                                       vp, fp, vp, vp, fp, fp, fp, fp, vp, fp, fp, vp, sz, vp]
         lib.mamba_state_update.restype = ctypes.c_int
         lib.mamba_state_update.argtypes = [ctypes.POINTER(Desc), fp, vp, vp, fp, vp, vp, fp, vp, fp,
                                            vp, vp]
@@ -167,6 +172,67 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
                                      ctypes.c_size_t(ws_bytes), _stream(dev))
     _check(lib, st)
     return out, last_state
+
+
+def bwd_workspace_size(batch, seqlen, dim, dstate, io_dtype=torch.bfloat16, segments=0) -> int:
+    """Bytes of workspace mamba_scan_bwd needs on the current device."""
+    lib = load_library()
+    d = Desc(batch, seqlen, dim, dstate, _IO[io_dtype], int(segments))
+    return int(lib.mamba_scan_bwd_workspace_size(ctypes.byref(d)))
+
+
+def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, *, h0=None, dlast=None,
+             segments=0, want_dz=True, want_dh0=True):
+    """Gradients of scan_fwd(x, delta, A, B, C, D, z, delta_bias, h0=h0) for
+    dLoss/dout = dout (batch, L, dim, x's dtype) and dLoss/d(last_state) =
+    dlast ((batch, dim, N) float32 or None). Returns a dict with dx, ddelta,
+    dz (batch, L, dim) in x's dtype (dz None without z or want_dz), dA (dim,
+    N), dB, dC (batch, L, N), dD, ddelta_bias (dim,) and dh0 (batch, dim, N,
+    None unless want_dh0), all float32 except dx, ddelta, dz."""
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, dim) and A (dim, N)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("scan_bwd runs on a GPU tensor")
+    io = x.dtype
+    if io not in _IO:
+        raise TypeError(f"unsupported io dtype {io}")
+    _need(x, "x", (batch, L, dim), io, dev)
+    _need(delta, "delta", (batch, L, dim), io, dev)
+    _need(z, "z", (batch, L, dim), io, dev)
+    _need(dout, "dout", (batch, L, dim), io, dev)
+    _need(B, "B", (batch, L, N), io, dev)
+    _need(C, "C", (batch, L, N), io, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _need(h0, "h0", (batch, dim, N), torch.float32, dev)
+    _need(dlast, "dlast", (batch, dim, N), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {
+        "dx": torch.empty((batch, L, dim), dtype=io, device=dev),
+        "ddelta": torch.empty((batch, L, dim), dtype=io, device=dev),
+        "dz": torch.empty((batch, L, dim), dtype=io, device=dev) if (z is not None and want_dz) else None,
+        "dA": torch.empty((dim, N), **f32),
+        "dB": torch.empty((batch, L, N), **f32),
+        "dC": torch.empty((batch, L, N), **f32),
+        "dD": torch.empty((dim,), **f32),
+        "ddelta_bias": torch.empty((dim,), **f32),
+        "dh0": torch.empty((batch, dim, N), **f32) if want_dh0 else None,
+    }
+    d = Desc(batch, L, dim, N, _IO[io], int(segments))
+    ws_bytes = int(lib.mamba_scan_bwd_workspace_size(ctypes.byref(d)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.mamba_scan_bwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(dlast),
+                            _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                            _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
+                            _ptr(g["dh0"]), _ptr(ws), ctypes.c_size_t(ws_bytes), _stream(dev))
+    _check(lib, st)
+    return g
 
 
 def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None):

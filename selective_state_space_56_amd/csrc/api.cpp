@@ -1,6 +1,7 @@
 // C ABI of the selective scan library: argument validation, planning and
 // dispatch to the HIP kernels. See include/mamba_scan.h for the contract.
 #include "mamba_scan.h"
+#include "mamba_scan_bwd.h"
 #include "mamba_conv.h"
 
 #include <hip/hip_runtime_api.h>
@@ -429,6 +430,147 @@ mamba_status mamba_conv1d_update(const mamba_conv_desc* d, void* state, const vo
   p.width = static_cast<int>(W);
   p.io = d->io_dtype;
   const hipError_t e = mscan::launch_conv1d_update(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+mamba_status scan_bwd_check(const char* who, const mamba_scan_desc* d) {
+  mamba_status st = check_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  if (d->flags & ~0xffffu)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
+  return MAMBA_OK;
+}
+
+mscan::ScanBwdPlan bwd_plan(const mamba_scan_desc* d) {
+  return mscan::plan_scan_bwd(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
+                              forced_segments(d));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc* d) {
+  if (!d || check_desc(d, "mamba_scan_bwd_workspace_size") != MAMBA_OK || (d->flags & ~0xffffu))
+    return 0;
+  return bwd_plan(d).workspace_bytes;
+}
+
+mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void* delta,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const void* z, const float* delta_bias, const float* h0,
+                            const void* dout, const float* dlast, void* dx, void* ddelta,
+                            float* dA, float* dB, float* dC, float* dD, void* dz,
+                            float* ddelta_bias, float* dh0, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const char* who = "mamba_scan_bwd";
+  mamba_status st = scan_bwd_check(who, d);
+  if (st != MAMBA_OK) return st;
+  const int64_t rows = d->batch * d->dim;
+  const int64_t tokens = d->batch * d->seqlen;
+  const int64_t elems = tokens * d->dim;
+  if (d->dim == 0) return ok();
+  if (!dA) return fail(MAMBA_ERR_INVALID_ARG, "%s: dA is NULL", who);
+  if (elems > 0) {
+    const struct {
+      const char* name;
+      const void* p;
+    } req[] = {{"x", x},       {"delta", delta},   {"A", A},   {"B", B},   {"C", C},
+               {"dout", dout}, {"dx", dx},         {"ddelta", ddelta},     {"dB", dB},
+               {"dC", dC}};
+    for (const auto& r : req)
+      if (!r.p) return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is NULL", who, r.name);
+  }
+  const mscan::ScanBwdPlan plan = bwd_plan(d);
+  if (elems > 0) {
+    if (!workspace)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who,
+                  plan.workspace_bytes);
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace has %zu bytes, %zu needed", who,
+                  workspace_bytes, plan.workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", who);
+  }
+  const size_t eb = io_bytes(d->io_dtype);
+  const size_t N = static_cast<size_t>(d->dstate);
+  const size_t E = static_cast<size_t>(elems) * eb;
+  const Span in[] = {
+      {"x", x, E},
+      {"delta", delta, E},
+      {"z", z, E},
+      {"dout", dout, E},
+      {"B", B, static_cast<size_t>(tokens) * N * eb},
+      {"C", C, static_cast<size_t>(tokens) * N * eb},
+      {"A", A, static_cast<size_t>(d->dim) * N * 4},
+      {"D", D, static_cast<size_t>(d->dim) * 4},
+      {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
+      {"h0", h0, static_cast<size_t>(rows) * N * 4},
+      {"dlast", dlast, static_cast<size_t>(rows) * N * 4},
+  };
+  const Span out[] = {
+      {"dx", dx, E},
+      {"ddelta", ddelta, E},
+      {"dz", z ? dz : nullptr, E},
+      {"dA", dA, static_cast<size_t>(d->dim) * N * 4},
+      {"dB", dB, static_cast<size_t>(tokens) * N * 4},
+      {"dC", dC, static_cast<size_t>(tokens) * N * 4},
+      {"dD", dD, static_cast<size_t>(d->dim) * 4},
+      {"ddelta_bias", ddelta_bias, static_cast<size_t>(d->dim) * 4},
+      {"dh0", dh0, static_cast<size_t>(rows) * N * 4},
+      {"workspace", elems > 0 ? workspace : nullptr, plan.workspace_bytes},
+  };
+  const size_t n_out = sizeof(out) / sizeof(out[0]);
+  for (size_t i = 0; i < n_out; ++i) {
+    for (const Span& s : in)
+      if (overlaps(out[i], s))
+        return fail(MAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", who, out[i].name, s.name);
+    for (size_t j = i + 1; j < n_out; ++j)
+      if (overlaps(out[i], out[j]))
+        return fail(MAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", who, out[i].name, out[j].name);
+  }
+  if ((st = check_align(who, {in[0], in[1], in[2], in[3], out[0], out[1], out[2]}, eb)) != MAMBA_OK)
+    return st;
+  const size_t bc_align = (eb == 2 && N == 1) ? 2 : 4;
+  if ((st = check_align(who, {in[4], in[5]}, bc_align)) != MAMBA_OK) return st;
+  if ((st = check_align(who, {in[6], in[7], in[8], in[9], in[10], out[3], out[4], out[5], out[6],
+                              out[7], out[8]},
+                        4)) != MAMBA_OK)
+    return st;
+
+  mscan::ScanBwdProblem p;
+  p.x = x;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.bias = delta_bias;
+  p.h0 = h0;
+  p.dout = dout;
+  p.dlast = dlast;
+  p.dx = dx;
+  p.ddelta = ddelta;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dz = z ? dz : nullptr;
+  p.dbias = ddelta_bias;
+  p.dh0 = dh0;
+  p.batch = d->batch;
+  p.seqlen = d->seqlen;
+  p.dim = d->dim;
+  p.dstate = static_cast<int>(d->dstate);
+  p.io = d->io_dtype;
+  const hipError_t e = mscan::launch_scan_bwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

@@ -41,6 +41,60 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
 hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* workspace,
                            hipStream_t stream);
 
+// The first two launches of launch_scan_fwd alone (out and last_state are not
+// touched). Afterwards, in stream order, the workspace starts with the state
+// entering every segment s >= 1: float[segments - 1][batch * dim][dstate], slot
+// s - 1 for segment s (nothing when plan.segments < 2).
+hipError_t launch_scan_carries(const ScanProblem& p, const ScanPlan& plan, void* workspace,
+                               hipStream_t stream);
+
+// Compute units of the current HIP device (256 when it cannot be queried).
+int device_cu_count();
+
+// Backward of the full-sequence scan: gradients for dLoss/dy = dout and
+// optionally dLoss/d(final state) = dlast. dx, ddelta, dz in the io dtype;
+// every other gradient fp32. Nullable: z (no gate), dz, D, bias, h0, dlast,
+// dD, dbias, dh0.
+struct ScanBwdProblem {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* h0;
+  const void* dout;
+  const float* dlast;
+  void* dx;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  void* dz;
+  float* dbias;
+  float* dh0;
+  int64_t batch, seqlen, dim;
+  int dstate;
+  int io;
+};
+
+// Segmentation (shared with the forward carries, whose workspace comes first)
+// and byte offsets of the backward's workspace regions.
+struct ScanBwdPlan {
+  ScanPlan seg;
+  size_t adj_off, ck_off, pa_off, pdb_off, pbc_off;
+  size_t workspace_bytes;
+};
+
+ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                          int forced_segments);
+
+hipError_t launch_scan_bwd(const ScanBwdProblem& p, const ScanBwdPlan& plan, void* workspace,
+                           hipStream_t stream);
+
 struct DecodeProblem {
   float* state;
   const void* x;

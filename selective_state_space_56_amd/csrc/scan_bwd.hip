@@ -1,0 +1,840 @@
+// Backward of the full-sequence selective scan (S6) on gfx950: the gradients
+// of a loss with respect to x, Delta_raw, A, B, C, D, z, the Delta bias and the
+// initial state, given dLoss/dy and optionally dLoss/d(final state).
+//
+// The states are not kept from the forward pass; they are recomputed here from
+// the inputs (erikxu.me notes "Mamba: Linear-Time Sequence Modeling with
+// Selective State Spaces", section "GPU Memory Hierarchy"; "Mamba and
+// selective state spaces, from first principles", section "The hardware-aware
+// scan").
+//
+// Reverse-mode differentiation of h_t = abar_t h_{t-1} + Delta_t B_t x_t,
+// abar_t = exp(Delta_t A), y_t = (C_t . h_t + D x_t) silu(z_t), per row (b, d)
+// and state n:
+//   ds_t     = dy_t silu(z_t)                        gradient of the pre-gate output
+//   lam_t    = C_t ds_t + abar_{t+1} lam_{t+1},       lam_{L-1} = C_{L-1} ds_{L-1} + dlast
+//   dA      += Delta_t lam_t abar_t h_{t-1}
+//   dDelta_t = sum_n lam_t,n (A_n abar_t,n h_{t-1},n + B_t,n x_t)
+//   dx_t     = D ds_t + Delta_t sum_n lam_t,n B_t,n
+//   dB_t,n  += lam_t,n Delta_t x_t                   (summed over channels)
+//   dC_t,n  += ds_t h_t,n                            (summed over channels)
+//   dD      += ds_t x_t,   dz_t = dy_t (C_t . h_t + D x_t) silu'(z_t)
+//   dDelta_raw_t = dDelta_t sigmoid(Delta_raw_t + bias),   dbias += dDelta_raw_t
+//   dh0      = abar_0 lam_0
+//
+// Time is cut into segments as in the forward scan. Launches, in order:
+//   F. the forward scan's aggregate and combine: every segment's carry-in state;
+//   1. adjoint aggregate: every segment but the first runs the adjoint
+//      recurrence backwards from zero and records abar at its first step times
+//      the adjoint there, and its sum of Delta;
+//   2. adjoint fold: a reverse fold over segments per (row, n), from dlast,
+//      gives the adjoint that enters each segment from later time (the affine
+//      pair combine of the forward scan run backwards: over a segment the
+//      adjoint decays by exp(A_n sum Delta));
+//   3. main: each segment scans forward from its carry-in and stores the state
+//      at the start of every chunk of kChunk steps (checkpoints, in the
+//      workspace), then walks its chunks backwards: it recomputes the chunk's
+//      states from the checkpoint into registers and steps the adjoint back
+//      through them, writing dx, dDelta_raw and dz and accumulating dA, dD and
+//      dbias per lane; dB and dC of a step are summed over the wave's channels
+//      with cross-lane exchanges, then over the workgroup's waves in LDS, and
+//      stored per channel tile;
+//   4. sums of the per-(segment, batch row) dA, dD, dbias partials and of the
+//      per-tile dB, dC partials.
+#include "device_math.h"
+#include "kernels.h"
+#include "tile_io.h"
+
+namespace mscan {
+
+namespace {
+
+struct BwdDims {
+  int64_t batch, seqlen, dim, rows, seg_len;
+  int segments;
+  unsigned tiles;
+};
+
+// Pointers of one backward call. carry_h: forward carry-in states (slot s - 1
+// for segment s); carry_a: adjoint aggregates, then (after the fold) the
+// adjoint entering segment s from later time in slot s; ck: checkpoints; pA,
+// pDb, pBC: partial sums.
+struct BwdPtrs {
+  const void* x;
+  const void* delta;
+  const void* B;
+  const void* C;
+  const void* z;
+  const void* dy;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* h0;
+  const float* dlast;
+  void* dx;
+  void* ddelta;
+  void* dz;
+  float* dh0;
+  const float* carry_h;
+  float* carry_a;
+  float* carry_s;
+  float* ck;
+  float* pA;
+  float* pDb;
+  float* pBC;
+};
+
+__device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+template <int M>
+constexpr int log2_of() {
+  int k = 0;
+  while ((1 << k) < M) ++k;
+  return k;
+}
+
+// Sums M values (M a power of two, at most 64) over the 64 lanes of a wave by
+// recursive halving: at level k, lane l keeps one half of its values, sends
+// the other half to lane l ^ 2^k and adds what that lane sends back. Lane l
+// returns the wave total of value scatter_index<M>(l). Each level is its own
+// instantiation so that every array index is a compile-time constant.
+template <int M, int K>
+__device__ __forceinline__ void sum_scatter_level(float (&v)[M], int lane) {
+  constexpr int H = M >> (K + 1);
+  if constexpr (H >= 1) {
+    const bool hi = (lane >> K) & 1;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float keep = hi ? v[i + H] : v[i];
+      const float send = hi ? v[i] : v[i + H];
+      v[i] = keep + __shfl_xor(send, 1 << K);
+    }
+    sum_scatter_level<M, K + 1>(v, lane);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ float wave_sum_scatter(float (&v)[M], int lane) {
+  sum_scatter_level<M, 0>(v, lane);
+  float r = v[0];
+#pragma unroll
+  for (int k = log2_of<M>(); k < 6; ++k) r += __shfl_xor(r, 1 << k);
+  return r;
+}
+
+template <int M>
+__device__ __forceinline__ int scatter_index(int lane) {
+  constexpr int kLevels = log2_of<M>();
+  int e = 0;
+#pragma unroll
+  for (int k = 0; k < kLevels; ++k) e += ((lane >> k) & 1) * (M >> (k + 1));
+  return e;
+}
+
+// LDS staging of one chunk: NIN input tiles (raw io values), the chunk's B and
+// C widened to fp32, NOUT output tiles and the per-wave dB/dC sums (double
+// buffered where a chunk is fetched or stored while another is computed).
+template <int N, class IO, int NIN, int NOUT>
+struct __align__(16) BwdStage {
+  typename IO::raw in[2][NIN][kChunk][kBlock];
+  float bc[2][kChunk][2 * N];
+  typename IO::raw go[NOUT ? 2 : 1][NOUT ? NOUT : 1][NOUT ? kChunk : 1][kBlock];
+  float red[NOUT ? kBlock / 64 : 1][NOUT ? kChunk : 1][2 * N];
+};
+
+// Addressing of one workgroup's channel tile within one time segment, shared
+// by the adjoint aggregate and the main kernel.
+template <int N, class IO, int CW>
+struct TileCtx {
+  using raw = typename IO::raw;
+  static constexpr int eb = sizeof(raw);
+  static constexpr int kTileElems = kChunk * 2 * N;
+  static constexpr int kBcPer = (kTileElems + kBlock - 1) / kBlock;
+  int64_t b, d0, d, row, row0, t_begin;
+  uint32_t steps, row_bytes, ch_off, lane_off;
+  unsigned tile;
+  int s, wv;
+  bool active;
+  const raw* Bp;
+  const raw* Cp;
+  BcOffsets bco[kBcPer];
+
+  __device__ __forceinline__ TileCtx(const BwdDims& g, const void* B, const void* C, int seg) {
+    const int tid = threadIdx.x;
+    b = blockIdx.x / g.tiles;
+    tile = blockIdx.x % g.tiles;
+    d0 = static_cast<int64_t>(tile) * kBlock;
+    active = d0 + tid < g.dim;
+    // lanes past the last channel compute on channel dim - 1 and store nothing
+    d = active ? d0 + tid : g.dim - 1;
+    s = seg;
+    t_begin = static_cast<int64_t>(s) * g.seg_len;
+    const int64_t t_end = t_begin + g.seg_len < g.seqlen ? t_begin + g.seg_len : g.seqlen;
+    steps = static_cast<uint32_t>(t_end - t_begin);
+    row = b * g.dim + d;
+    row0 = (b * g.seqlen + t_begin) * g.dim + d0;
+    row_bytes = static_cast<uint32_t>(g.dim * eb);
+    const int64_t left = g.dim - d0;
+    const uint32_t valid_bytes = static_cast<uint32_t>((left < kBlock ? left : kBlock) * eb);
+    ch_off = active ? tid * eb : kOffNone;
+    lane_off = CW != 0 ? tile_lane_offset<IO, (CW != 0 ? CW : 4)>(row_bytes, valid_bytes) : 0u;
+    wv = __builtin_amdgcn_readfirstlane(tid / 64);
+    Bp = static_cast<const raw*>(B) + (b * g.seqlen + t_begin) * N;
+    Cp = static_cast<const raw*>(C) + (b * g.seqlen + t_begin) * N;
+#pragma unroll
+    for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock);
+  }
+
+  // Start copying the tile rows of chunk step t1 of `count` tensors into the
+  // consecutive tiles (kChunk x kBlock each) from `tiles` on (register-staged:
+  // into regs[k], written by land()).
+  static constexpr int kTile = kChunk * kBlock;
+  template <int NT>
+  __device__ __forceinline__ void fetch(const raw* const (&src)[NT], int count, uint32_t t1,
+                                        raw* tiles, TileRegs<IO> (&regs)[NT]) const {
+    const int64_t at = static_cast<int64_t>(t1) * (row_bytes / eb);
+    const uint32_t left = steps - t1;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      if (k < count) {
+        if constexpr (CW != 0)
+          dma_tile<IO, CW>(src[k] + at, left, row_bytes, tiles + k * kTile, wv, lane_off);
+        else
+          load_tile_regs<IO>(regs[k], src[k] + at, left, row_bytes, ch_off);
+      }
+    }
+  }
+  template <int NT>
+  __device__ __forceinline__ void land(int count, raw* tiles, const TileRegs<IO> (&regs)[NT]) const {
+    if constexpr (CW == 0) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k)
+        if (k < count) store_tile_regs<IO>(regs[k], tiles + k * kTile);
+    }
+  }
+  __device__ __forceinline__ void fetch_bc(uint32_t t1, float (&bcv)[kBcPer]) const {
+#pragma unroll
+    for (int r = 0; r < kBcPer; ++r)
+      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
+                              steps - t1, bco[r]);
+  }
+  __device__ __forceinline__ void land_bc(const float (&bcv)[kBcPer], float (*bc)[2 * N]) const {
+#pragma unroll
+    for (int r = 0; r < kBcPer; ++r) {
+      const int i = threadIdx.x + r * kBlock;
+      if (i < kTileElems) bc[i / (2 * N)][i % (2 * N)] = bcv[r];
+    }
+  }
+};
+
+// Workgroups per CU: the adjoint aggregate as many as fit its LDS staging
+// (bf16 tiles are half the size of fp32 ones); the main pass one, whose
+// registers (a chunk of recomputed states and the adjoint) take the whole
+// register file of a SIMD. The launch bounds hold the compiler to the matching
+// register budget.
+template <class IO>
+constexpr int kAggBlocksPerCU = sizeof(typename IO::raw) == 2 ? 4 : 3;
+#ifndef MSCAN_BWD_BLOCKS
+#define MSCAN_BWD_BLOCKS 1
+#endif
+template <class IO>
+constexpr int kMainBlocksPerCU = sizeof(typename IO::raw) == 2 ? MSCAN_BWD_BLOCKS : 1;
+
+// ---------------------------------------------------------------------------
+// 1. Adjoint aggregate. Grid: x = batch * channel tiles, y = segment - 1.
+// Runs the adjoint recurrence of segment blockIdx.y + 1 backwards from zero;
+// stores abar at the segment's first step times the adjoint there, and the
+// segment's sum of Delta, in slot blockIdx.y.
+template <int N, class IO, bool GATE, int CW>
+__global__ __launch_bounds__(kBlock, kAggBlocksPerCU<IO>) void bwd_adjoint_aggregate_kernel(BwdPtrs a, BwdDims g) {
+  using raw = typename IO::raw;
+  constexpr int kIn = GATE ? 3 : 2;  // Delta_raw, dy (, z)
+  __shared__ BwdStage<N, IO, kIn, 0> st;
+  const int tid = threadIdx.x;
+  const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y + 1);
+
+  float A2[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) A2[n] = a.A[tc.d * N + n] * kLog2e;
+  const float bias = a.bias ? a.bias[tc.d] : 0.0f;
+
+  const raw* const src[3] = {static_cast<const raw*>(a.delta) + tc.row0,
+                             static_cast<const raw*>(a.dy) + tc.row0,
+                             static_cast<const raw*>(GATE ? a.z : a.dy) + tc.row0};
+  TileRegs<IO> regs[3];
+  float bcv[TileCtx<N, IO, CW>::kBcPer];
+
+  float m[N];  // abar_{t+1} lam_{t+1}
+#pragma unroll
+  for (int n = 0; n < N; ++n) m[n] = 0.0f;
+  float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta
+
+  const int last = static_cast<int>((tc.steps + kChunk - 1) / kChunk) - 1;
+  {
+    const int nb = last & 1;
+    tc.fetch(src, kIn, last * kChunk, &st.in[nb][0][0][0], regs);
+    tc.fetch_bc(last * kChunk, bcv);
+    tc.land(kIn, &st.in[nb][0][0][0], regs);
+    tc.land_bc(bcv, st.bc[nb]);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int c = last; c >= 0; --c) {
+    const int buf = c & 1;
+    if (c > 0) {
+      tc.fetch(src, kIn, (c - 1) * kChunk, &st.in[buf ^ 1][0][0][0], regs);
+      tc.fetch_bc((c - 1) * kChunk, bcv);
+    }
+    const int valid = static_cast<int>(tc.steps) - c * kChunk;
+    float dsum = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < kChunk; ++jj) {
+      const int j = kChunk - 1 - jj;
+      if (j < valid) {
+        const float Delta = softplus_f(IO::to_f32(st.in[buf][0][j][tid]) + bias);
+        const float dyv = IO::to_f32(st.in[buf][1][j][tid]);
+        const float ds = GATE ? dyv * silu_f(IO::to_f32(st.in[buf][kIn - 1][j][tid])) : dyv;
+        const float* Cr = &st.bc[buf][j][N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const float lam = fmaf(Cr[n], ds, m[n]);
+          m[n] = hw_exp2(Delta * A2[n]) * lam;
+        }
+        dsum += Delta;
+      }
+    }
+    const float v = dsum - S_c;
+    const float tsum = S + v;
+    S_c = (tsum - S) - v;
+    S = tsum;
+    if (c > 0) {
+      tc.land(kIn, &st.in[buf ^ 1][0][0][0], regs);
+      tc.land_bc(bcv, st.bc[buf ^ 1]);
+      wait_vmem();
+    }
+    __syncthreads();
+  }
+  if (!tc.active) return;
+  const int64_t slot = static_cast<int64_t>(blockIdx.y) * g.rows + tc.row;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.carry_a[slot * N + n] = m[n];
+  a.carry_s[slot] = S;
+}
+
+// ---------------------------------------------------------------------------
+// 2. Adjoint fold over segments, per (row, n), from the last segment back:
+// nu_{S-1} = dlast (or 0), nu_{s-1} = E_s + exp(A sum_s Delta) nu_s, where slot
+// s - 1 holds (E_s, sum_s Delta) on entry and nu_{s-1} on exit.
+constexpr int kFoldBlock = 8;
+
+template <int N>
+__global__ __launch_bounds__(kAuxBlock) void bwd_adjoint_fold_kernel(const float* __restrict__ A,
+                                                                  float* __restrict__ ws_e,
+                                                                  const float* __restrict__ ws_s,
+                                                                  const float* __restrict__ dlast,
+                                                                  int64_t rows, int64_t dim,
+                                                                  int segments) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
+  if (i >= rows * N) return;
+  const int64_t row = i / N;
+  const int n = static_cast<int>(i % N);
+  const float a2 = A[(row % dim) * N + n] * kLog2e;
+  float nu = dlast ? dlast[i] : 0.0f;
+  for (int k0 = segments - 2; k0 >= 0; k0 -= kFoldBlock) {
+    float ev[kFoldBlock], sv[kFoldBlock];
+#pragma unroll
+    for (int u = 0; u < kFoldBlock; ++u) {
+      const int k = k0 - u >= 0 ? k0 - u : 0;
+      ev[u] = ws_e[static_cast<int64_t>(k) * rows * N + i];
+      sv[u] = ws_s[static_cast<int64_t>(k) * rows + row];
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBlock; ++u) {
+      if (k0 - u >= 0) {
+        nu = fmaf(hw_exp2(a2 * sv[u]), nu, ev[u]);
+        ws_e[static_cast<int64_t>(k0 - u) * rows * N + i] = nu;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Main pass. Grid: x = batch * channel tiles, y = segment.
+// Checkpoint layout: float[chunk][N / 4][rows][4] (N >= 4) or
+// float[chunk][N][rows]: the state before the chunk's first step, for every
+// chunk of kChunk steps of the sequence.
+template <int N>
+__device__ __forceinline__ void ck_store(float* ck, int64_t chunk, int64_t rows, int64_t row,
+                                         const float (&v)[N]) {
+  float* base = ck + chunk * rows * N;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      *reinterpret_cast<float4*>(base + (q * rows + row) * 4) =
+          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) base[n * rows + row] = v[n];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void ck_load(const float* ck, int64_t chunk, int64_t rows, int64_t row,
+                                        float (&v)[N]) {
+  const float* base = ck + chunk * rows * N;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 w = *reinterpret_cast<const float4*>(base + (q * rows + row) * 4);
+      v[4 * q] = w.x;
+      v[4 * q + 1] = w.y;
+      v[4 * q + 2] = w.z;
+      v[4 * q + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = base[n * rows + row];
+  }
+}
+
+template <int N, class IO, bool GATE, int CW>
+__global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(BwdPtrs a, BwdDims g) {
+  using raw = typename IO::raw;
+  constexpr int M = 2 * N;
+  constexpr int kIn = GATE ? 4 : 3;   // x, Delta_raw, dy (, z)
+  constexpr int kOut = GATE ? 3 : 2;  // dx, dDelta_raw (, dz)
+  constexpr int iX = 0, iDl = 1, iDy = 2, iZ = 3;
+  __shared__ BwdStage<N, IO, kIn, kOut> st;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y);
+  const int s = tc.s;
+
+  float A2[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) A2[n] = a.A[tc.d * N + n] * kLog2e;
+  const float Dd = a.D ? a.D[tc.d] : 0.0f;
+  const float bias = a.bias ? a.bias[tc.d] : 0.0f;
+
+  const raw* const src[4] = {static_cast<const raw*>(a.x) + tc.row0,
+                             static_cast<const raw*>(a.delta) + tc.row0,
+                             static_cast<const raw*>(a.dy) + tc.row0,
+                             static_cast<const raw*>(GATE ? a.z : a.dy) + tc.row0};
+  TileRegs<IO> regs[4];
+  float bcv[TileCtx<N, IO, CW>::kBcPer];
+  raw* const dst[3] = {static_cast<raw*>(a.dx) + tc.row0, static_cast<raw*>(a.ddelta) + tc.row0,
+                       static_cast<raw*>(GATE && a.dz ? a.dz : a.dx) + tc.row0};
+  const int n_out = GATE && a.dz ? 3 : 2;
+  auto put = [&](int ob, uint32_t t1) {
+    const int64_t at = static_cast<int64_t>(t1) * g.dim;
+#pragma unroll
+    for (int k = 0; k < kOut; ++k)
+      if (k < n_out)
+        store_tile<IO, CW>(dst[k] + at, tc.steps - t1, tc.row_bytes, &st.go[ob][k][0][0],
+                           tc.lane_off, tc.ch_off);
+  };
+
+  const int last = static_cast<int>((tc.steps + kChunk - 1) / kChunk) - 1;
+  const int64_t ck0 = tc.t_begin / kChunk;  // sequence chunk index of the segment's chunk 0
+
+  // Forward sweep from the carry-in: checkpoint at every chunk start.
+  float h[N];
+  if (s > 0) {
+    const float* hin = a.carry_h + (static_cast<int64_t>(s - 1) * g.rows + tc.row) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = hin[n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = a.h0 ? a.h0[tc.row * N + n] : 0.0f;
+  }
+  tc.fetch(src, 2, 0, &st.in[0][0][0][0], regs);
+  tc.fetch_bc(0, bcv);
+  tc.land(2, &st.in[0][0][0][0], regs);
+  tc.land_bc(bcv, st.bc[0]);
+  wait_vmem();
+  __syncthreads();
+  for (int c = 0; c <= last; ++c) {
+    const int buf = c & 1;
+    if (c < last) {
+      tc.fetch(src, 2, (c + 1) * kChunk, &st.in[buf ^ 1][0][0][0], regs);
+      tc.fetch_bc((c + 1) * kChunk, bcv);
+    }
+    if (tc.active) ck_store<N>(a.ck, ck0 + c, g.rows, tc.row, h);
+    const int valid = static_cast<int>(tc.steps) - c * kChunk;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < valid) {
+        const float xf = IO::to_f32(st.in[buf][iX][j][tid]);
+        const float Delta = softplus_f(IO::to_f32(st.in[buf][iDl][j][tid]) + bias);
+        const float dxv = Delta * xf;
+        const float* Br = &st.bc[buf][j][0];
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = fmaf(hw_exp2(Delta * A2[n]), h[n], dxv * Br[n]);
+      }
+    }
+    if (c < last) {
+      tc.land(2, &st.in[buf ^ 1][0][0][0], regs);
+      tc.land_bc(bcv, st.bc[buf ^ 1]);
+      wait_vmem();
+    }
+    __syncthreads();
+  }
+
+  // Reverse sweep over the chunks.
+  float m[N];  // abar_{t+1} lam_{t+1}: the adjoint entering from later time
+  if (s + 1 < g.segments) {
+    const float* ain = a.carry_a + (static_cast<int64_t>(s) * g.rows + tc.row) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) m[n] = ain[n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) m[n] = a.dlast ? a.dlast[tc.row * N + n] : 0.0f;
+  }
+  float dA[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) dA[n] = 0.0f;
+  float dD = 0.0f, dbias = 0.0f;
+  const int e_idx = scatter_index<M>(lane);
+  float* pbc = a.pBC + ((static_cast<int64_t>(tc.tile) * g.batch + tc.b) * g.seqlen + tc.t_begin) * M;
+
+  {
+    const int nb = last & 1;
+    tc.fetch(src, kIn, last * kChunk, &st.in[nb][0][0][0], regs);
+    tc.fetch_bc(last * kChunk, bcv);
+    tc.land(kIn, &st.in[nb][0][0][0], regs);
+    tc.land_bc(bcv, st.bc[nb]);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int c = last; c >= 0; --c) {
+    const int buf = c & 1;
+    if (c < last) put(buf ^ 1, (c + 1) * kChunk);
+    if (c > 0) {
+      tc.fetch(src, kIn, (c - 1) * kChunk, &st.in[buf ^ 1][0][0][0], regs);
+      tc.fetch_bc((c - 1) * kChunk, bcv);
+    }
+    float hc[N];  // state before the chunk's first step
+    ck_load<N>(a.ck, ck0 + c, g.rows, tc.row, hc);
+    const int valid = static_cast<int>(tc.steps) - c * kChunk;
+    // recompute the chunk's states
+    float hist[kChunk][N];
+    float Dl[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < valid) {
+        const float xf = IO::to_f32(st.in[buf][iX][j][tid]);
+        const float Delta = softplus_f(IO::to_f32(st.in[buf][iDl][j][tid]) + bias);
+        Dl[j] = Delta;
+        const float dxv = Delta * xf;
+        const float* Br = &st.bc[buf][j][0];
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+          hist[j][n] = fmaf(hw_exp2(Delta * A2[n]), j == 0 ? hc[n] : hist[j - 1][n], dxv * Br[n]);
+      }
+    }
+    // step the adjoint back through them
+#pragma unroll
+    for (int jj = 0; jj < kChunk; ++jj) {
+      const int j = kChunk - 1 - jj;
+      if (j < valid) {
+        const float xf = IO::to_f32(st.in[buf][iX][j][tid]);
+        const float u = IO::to_f32(st.in[buf][iDl][j][tid]) + bias;
+        const float Delta = Dl[j];
+        const float dyv = IO::to_f32(st.in[buf][iDy][j][tid]);
+        float zf = 0.0f, sz = 0.0f, ds = dyv;
+        if (GATE) {
+          zf = IO::to_f32(st.in[buf][iZ][j][tid]);
+          sz = sigmoid_f(zf);
+          ds = dyv * (zf * sz);
+        }
+        const float dxv = Delta * xf;
+        float bc[2 * N];
+        read_bc<N>(st.bc[buf][j], bc, true);
+        float sAq = 0.0f, sLB = 0.0f, ypre = Dd * xf;
+        float vals[M];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const float hprev = j == 0 ? hc[n] : hist[j - 1][n];
+          const float lam = fmaf(bc[N + n], ds, m[n]);
+          const float lp = hw_exp2(Delta * A2[n]) * lam;  // abar_t lam_t
+          const float q = lp * hprev;
+          dA[n] = fmaf(Delta, q, dA[n]);
+          sAq = fmaf(A2[n], q, sAq);
+          sLB = fmaf(lam, bc[n], sLB);
+          ypre = fmaf(bc[N + n], hist[j][n], ypre);
+          vals[n] = lam * dxv;
+          vals[N + n] = ds * hist[j][n];
+          m[n] = lp;
+        }
+#pragma unroll
+        for (int k = 0; k < M; ++k) vals[k] = tc.active ? vals[k] : 0.0f;
+        const float tot = wave_sum_scatter<M>(vals, lane);
+        if (lane < M) st.red[tc.wv][j][e_idx] = tot;
+        const float dDelta = fmaf(sAq, kLn2, xf * sLB);
+        const float ddr = dDelta * sigmoid_f(u);
+        dbias += ddr;
+        dD = fmaf(ds, xf, dD);
+        st.go[buf][0][j][tid] = IO::from_f32(fmaf(Dd, ds, Delta * sLB));
+        st.go[buf][1][j][tid] = IO::from_f32(ddr);
+        if (GATE) st.go[buf][kOut - 1][j][tid] = IO::from_f32(dyv * ypre * sz * fmaf(zf, 1.0f - sz, 1.0f));
+      }
+    }
+    __syncthreads();
+    // this chunk's dB / dC over the workgroup's channels
+    for (int i = tid; i < (valid < kChunk ? valid : kChunk) * M; i += kBlock) {
+      const int j = i / M, k = i % M;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kBlock / 64; ++w) sum += st.red[w][j][k];
+      pbc[static_cast<int64_t>(c * kChunk + j) * M + k] = sum;
+    }
+    if (c > 0) {
+      tc.land(kIn, &st.in[buf ^ 1][0][0][0], regs);
+      tc.land_bc(bcv, st.bc[buf ^ 1]);
+      wait_vmem();
+    }
+    __syncthreads();
+  }
+  put(0, 0);
+  if (!tc.active) return;
+  if (s == 0 && a.dh0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) a.dh0[tc.row * N + n] = m[n];
+  }
+  const int64_t part = static_cast<int64_t>(s) * g.batch + tc.b;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.pA[(part * g.dim + tc.d) * N + n] = dA[n];
+  a.pDb[(part * 2) * g.dim + tc.d] = dD;
+  a.pDb[(part * 2 + 1) * g.dim + tc.d] = dbias;
+}
+
+// ---------------------------------------------------------------------------
+// 4. Sums of the partials.
+// dA[d, n] = sum_p pA[p, d, n]; dD[d], dbias[d] likewise from pDb[p, 0 / 1, d].
+template <int N>
+__global__ __launch_bounds__(kAuxBlock) void bwd_param_sum_kernel(const float* __restrict__ pA,
+                                                               const float* __restrict__ pDb,
+                                                               float* __restrict__ dA,
+                                                               float* __restrict__ dD,
+                                                               float* __restrict__ dbias,
+                                                               int64_t dim, int64_t parts) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
+  const int64_t na = dim * N;
+  if (i < na) {
+    float acc = 0.0f;
+    for (int64_t p = 0; p < parts; ++p) acc += pA[p * na + i];
+    dA[i] = acc;
+  } else if (i < na + 2 * dim) {
+    const int64_t j = i - na;
+    const int64_t which = j / dim, d = j % dim;
+    float* outp = which == 0 ? dD : dbias;
+    if (!outp) return;
+    float acc = 0.0f;
+    for (int64_t p = 0; p < parts; ++p) acc += pDb[(p * 2 + which) * dim + d];
+    outp[d] = acc;
+  }
+}
+
+// dB[b, t, n] = sum over channel tiles of pBC[tile, b, t, n], dC from n + N.
+template <int N>
+__global__ __launch_bounds__(kAuxBlock) void bwd_bc_sum_kernel(const float* __restrict__ pBC,
+                                                            float* __restrict__ dB,
+                                                            float* __restrict__ dC,
+                                                            int64_t tokens, unsigned tiles) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
+  const int64_t total = tokens * 2 * N;
+  if (i >= total) return;
+  float acc = 0.0f;
+  for (unsigned k = 0; k < tiles; ++k) acc += pBC[static_cast<int64_t>(k) * total + i];
+  const int64_t tok = i / (2 * N);
+  const int k = static_cast<int>(i % (2 * N));
+  if (k < N)
+    dB[tok * N + k] = acc;
+  else
+    dC[tok * N + k - N] = acc;
+}
+
+// dst[i] = src[i], or 0 without src.
+__global__ __launch_bounds__(kAuxBlock) void bwd_fill_kernel(float* dst, const float* src,
+                                                             int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t fill(float* dst, const float* src, int64_t n, hipStream_t stream) {
+  if (!dst || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_fill_kernel, dim3(static_cast<unsigned>((n + kAuxBlock - 1) / kAuxBlock)),
+                     dim3(kAuxBlock), 0, stream, dst, src, n);
+  return hipGetLastError();
+}
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+template <int N, class IO, bool GATE, int CW>
+hipError_t launch_typed(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* ws,
+                        hipStream_t stream) {
+  BwdDims g;
+  g.batch = p.batch;
+  g.seqlen = p.seqlen;
+  g.dim = p.dim;
+  g.rows = p.batch * p.dim;
+  g.seg_len = plan.seg.seg_len;
+  g.segments = plan.seg.segments;
+  g.tiles = static_cast<unsigned>((p.dim + kBlock - 1) / kBlock);
+  BwdPtrs a;
+  a.x = p.x;
+  a.delta = p.delta;
+  a.B = p.B;
+  a.C = p.C;
+  a.z = p.z;
+  a.dy = p.dout;
+  a.A = p.A;
+  a.D = p.D;
+  a.bias = p.bias;
+  a.h0 = p.h0;
+  a.dlast = p.dlast;
+  a.dx = p.dx;
+  a.ddelta = p.ddelta;
+  a.dz = p.dz;
+  a.dh0 = p.dh0;
+  a.carry_h = reinterpret_cast<const float*>(ws);
+  a.carry_a = reinterpret_cast<float*>(ws + plan.adj_off);
+  a.carry_s = a.carry_a + static_cast<int64_t>(g.segments > 1 ? g.segments - 1 : 0) * g.rows * N;
+  a.ck = reinterpret_cast<float*>(ws + plan.ck_off);
+  a.pA = reinterpret_cast<float*>(ws + plan.pa_off);
+  a.pDb = reinterpret_cast<float*>(ws + plan.pdb_off);
+  a.pBC = reinterpret_cast<float*>(ws + plan.pbc_off);
+
+  const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
+  if (g.segments > 1) {
+    ScanProblem f;
+    f.x = p.x;
+    f.delta = p.delta;
+    f.A = p.A;
+    f.B = p.B;
+    f.C = p.C;
+    f.D = p.D;
+    f.z = p.z;
+    f.bias = p.bias;
+    f.h0 = p.h0;
+    f.out = nullptr;
+    f.last_state = nullptr;
+    f.batch = p.batch;
+    f.seqlen = p.seqlen;
+    f.dim = p.dim;
+    f.dstate = N;
+    f.io = p.io;
+    hipError_t e = launch_scan_carries(f, plan.seg, ws, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, IO, GATE, CW>),
+                       dim3(blocks, g.segments - 1), dim3(kBlock), 0, stream, a, g);
+    const int64_t work = g.rows * N;
+    hipLaunchKernelGGL((bwd_adjoint_fold_kernel<N>),
+                       dim3(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock)),
+                       dim3(kAuxBlock), 0, stream, p.A, a.carry_a, a.carry_s, p.dlast, g.rows, p.dim,
+                       g.segments);
+  }
+  hipLaunchKernelGGL((scan_bwd_kernel<N, IO, GATE, CW>), dim3(blocks, g.segments), dim3(kBlock), 0,
+                     stream, a, g);
+  const int64_t nparam = p.dim * N + 2 * p.dim;
+  hipLaunchKernelGGL((bwd_param_sum_kernel<N>),
+                     dim3(static_cast<unsigned>((nparam + kAuxBlock - 1) / kAuxBlock)),
+                     dim3(kAuxBlock), 0, stream, a.pA, a.pDb, p.dA, p.dD, p.dbias, p.dim,
+                     static_cast<int64_t>(g.segments) * p.batch);
+  const int64_t tokens = p.batch * p.seqlen;
+  const int64_t nbc = tokens * 2 * N;
+  hipLaunchKernelGGL((bwd_bc_sum_kernel<N>),
+                     dim3(static_cast<unsigned>((nbc + kAuxBlock - 1) / kAuxBlock)),
+                     dim3(kAuxBlock), 0, stream, a.pBC, p.dB, p.dC, tokens, g.tiles);
+  return hipGetLastError();
+}
+
+// Copy width of the tile moves (see the forward scan): every tensor moved
+// through a tile must allow it.
+template <int N, class IO, bool GATE>
+hipError_t launch_copy_width(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* ws,
+                             hipStream_t st) {
+  constexpr int eb = sizeof(typename IO::raw);
+  const void* ptrs[] = {p.x, p.delta, p.dout, p.z, p.dx, p.ddelta, p.dz};
+  bool a16 = (p.dim * eb) % 16 == 0, a4 = (p.dim * eb) % 4 == 0;
+  for (const void* q : ptrs) {
+    if (!q) continue;
+    a16 = a16 && reinterpret_cast<uintptr_t>(q) % 16 == 0;
+    a4 = a4 && reinterpret_cast<uintptr_t>(q) % 4 == 0;
+  }
+  if (a16) return launch_typed<N, IO, GATE, 16>(p, plan, ws, st);
+  if (a4) return launch_typed<N, IO, GATE, 4>(p, plan, ws, st);
+  return launch_typed<N, IO, GATE, 0>(p, plan, ws, st);
+}
+
+template <class IO, bool GATE>
+hipError_t dispatch_n(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* ws, hipStream_t st) {
+  switch (p.dstate) {
+    case 1: return launch_copy_width<1, IO, GATE>(p, plan, ws, st);
+    case 2: return launch_copy_width<2, IO, GATE>(p, plan, ws, st);
+    case 4: return launch_copy_width<4, IO, GATE>(p, plan, ws, st);
+    case 8: return launch_copy_width<8, IO, GATE>(p, plan, ws, st);
+    case 16: return launch_copy_width<16, IO, GATE>(p, plan, ws, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                          int forced_segments) {
+  ScanBwdPlan plan{};
+  const int64_t rows = batch * dim;
+  int segs = forced_segments;
+  if (segs <= 0 && rows > 0 && seqlen > 0) {
+    // Cut the sequence into enough segments for about two rounds of the main
+    // pass's resident workgroups, each at least 48 steps long.
+    const int64_t blocks = batch * ((dim + kBlock - 1) / kBlock);
+    const int64_t slots = static_cast<int64_t>(device_cu_count()) * kMainBlocksPerCU<Bf16Io>;
+    int64_t v = 2 * slots / blocks;
+    if (v > seqlen / 48) v = seqlen / 48;
+    segs = static_cast<int>(v < 1 ? 1 : (v > 4096 ? 4096 : v));
+  }
+  plan.seg = plan_scan(batch, seqlen, dim, dstate, segs > 0 ? segs : 1);
+  if (rows <= 0 || seqlen <= 0) return plan;
+  const size_t S = static_cast<size_t>(plan.seg.segments);
+  const size_t N = static_cast<size_t>(dstate);
+  const size_t R = static_cast<size_t>(rows);
+  const size_t tiles = static_cast<size_t>((dim + kBlock - 1) / kBlock);
+  const size_t chunks = static_cast<size_t>((seqlen + kChunk - 1) / kChunk);
+  size_t off = round256(plan.seg.workspace_bytes);
+  plan.adj_off = off;
+  off += round256((S - 1) * R * (N + 1) * sizeof(float));
+  plan.ck_off = off;
+  off += round256(chunks * R * N * sizeof(float));
+  plan.pa_off = off;
+  off += round256(S * R * N * sizeof(float));
+  plan.pdb_off = off;
+  off += round256(S * R * 2 * sizeof(float));
+  plan.pbc_off = off;
+  off += round256(tiles * static_cast<size_t>(batch) * static_cast<size_t>(seqlen) * 2 * N *
+                  sizeof(float));
+  plan.workspace_bytes = off;
+  return plan;
+}
+
+hipError_t launch_scan_bwd(const ScanBwdProblem& p, const ScanBwdPlan& plan, void* workspace,
+                           hipStream_t stream) {
+  if (p.dim == 0) return hipSuccess;
+  if (p.batch == 0 || p.seqlen == 0) {
+    // no steps: the adjoint passes through unchanged, every sum is empty
+    hipError_t e = fill(p.dA, nullptr, p.dim * p.dstate, stream);
+    if (e == hipSuccess) e = fill(p.dD, nullptr, p.dim, stream);
+    if (e == hipSuccess) e = fill(p.dbias, nullptr, p.dim, stream);
+    if (e == hipSuccess) e = fill(p.dh0, p.dlast, p.batch * p.dim * p.dstate, stream);
+    return e;
+  }
+  char* ws = static_cast<char*>(workspace);
+  if (p.io == kIoBf16)
+    return p.z ? dispatch_n<Bf16Io, true>(p, plan, ws, stream)
+               : dispatch_n<Bf16Io, false>(p, plan, ws, stream);
+  return p.z ? dispatch_n<F32Io, true>(p, plan, ws, stream)
+             : dispatch_n<F32Io, false>(p, plan, ws, stream);
+}
+
+}  // namespace mscan

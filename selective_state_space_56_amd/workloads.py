@@ -178,6 +178,16 @@ def make_decode_token(w: Workload, step: int, device="cpu", seed=0):
             "z": None if z is None else z.to(io)}
 
 
+def make_bwd_grads(w: Workload, device="cpu", seed=0):
+    """Incoming gradients for the backward pass: dout ~ N(0, 1) (batch, L, dim)
+    in the io dtype, and dlast ~ N(0, 1) (batch, dim, N) fp32 for the final
+    state."""
+    g = _gen(device, seed * 7919 + 3)
+    dout = torch.randn((w.batch, w.seqlen, w.dim), generator=g, device=device).to(w.torch_io)
+    dlast = torch.randn((w.batch, w.dim, w.dstate), generator=g, device=device)
+    return {"dout": dout, "dlast": dlast}
+
+
 def to_f64_numpy(t):
     """Exact widening of a (possibly bf16) tensor to a float64 numpy array."""
     if t is None:

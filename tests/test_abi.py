@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_init",
                           "mamba_state_update", "mamba_status_string", "mamba_last_error",
-                          "mamba_conv1d_fwd", "mamba_conv1d_update"}
+                          "mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd",
+                          "mamba_scan_bwd_workspace_size"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -240,3 +241,61 @@ def test_conv_update_validation(lib):
     assert conv_upd(lib, CD(seqlen=1), out=4) == INVALID     # out == state
     assert conv_upd(lib, CD(seqlen=1), state=1) == INVALID   # state == xin
     assert "state overlaps xin" in err(lib)
+
+
+BWD_ARGS = ["x", "delta", "A", "B", "C", "D", "z", "bias", "h0", "dout", "dlast", "dx", "ddelta",
+            "dA", "dB", "dC", "dD", "dz", "dbias", "dh0"]
+
+
+def bwd(lib, desc, ws=None, ws_bytes=0, **over):
+    """mamba_scan_bwd with every pointer a distinct fake address (argument k
+    at P(k + 1)) unless overridden (None = NULL)."""
+    ptrs = []
+    for k, name in enumerate(BWD_ARGS):
+        v = over.get(name, k + 1)
+        ptrs.append(None if v is None else (P(v) if isinstance(v, int) else v))
+    w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
+    return lib.mamba_scan_bwd(None if desc is None else ctypes.byref(desc), *ptrs, w,
+                              ctypes.c_size_t(ws_bytes), None)
+
+
+def test_scan_bwd_validation(lib):
+    d = D_(batch=1, seqlen=64, dim=16, flags=2)
+    need = lib.mamba_scan_bwd_workspace_size(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    assert lib.mamba_scan_bwd_workspace_size(None) == 0
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(D_(dstate=3))) == 0
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(D_(flags=1 << 16))) == 0
+    assert bwd(lib, None) == INVALID
+    assert "mamba_scan_bwd: desc is NULL" in err(lib)
+    assert bwd(lib, D_(dstate=32), ws=40, ws_bytes=need) == UNSUPPORTED
+    assert bwd(lib, D_(flags=1 << 20), ws=40, ws_bytes=need) == INVALID
+    for name in ["x", "delta", "A", "B", "C", "dout", "dx", "ddelta", "dA", "dB", "dC"]:
+        assert bwd(lib, d, ws=40, ws_bytes=need, **{name: None}) == INVALID, name
+        assert f"{name} is NULL" in err(lib)
+    assert bwd(lib, d, ws=None, ws_bytes=need) == INVALID          # workspace missing
+    assert "workspace" in err(lib)
+    assert bwd(lib, d, ws=40, ws_bytes=need - 256) == INVALID      # too small
+    assert "needed" in err(lib)
+    assert bwd(lib, d, ws=ctypes.c_void_p(FAKE + 0x100000 * 40 + 64), ws_bytes=need) == INVALID
+    assert "256-byte aligned" in err(lib)
+    # outputs must not overlap inputs, each other or the workspace
+    assert bwd(lib, d, ws=40, ws_bytes=need, dx=1) == INVALID
+    assert "dx overlaps x" in err(lib)
+    assert bwd(lib, d, ws=40, ws_bytes=need, dB=12) == INVALID
+    assert "overlaps" in err(lib)
+    assert bwd(lib, d, ws=40, ws_bytes=need, dh0=40) == INVALID
+    assert "dh0 overlaps workspace" in err(lib)
+    assert bwd(lib, d, ws=40, ws_bytes=need, dA=10) == INVALID      # dA == dout
+    odd = ctypes.c_void_p(FAKE + 0x100000 * 30 + 1)
+    assert bwd(lib, d, ws=40, ws_bytes=need, ddelta=odd) == INVALID
+    assert "aligned" in err(lib)
+    odd4 = ctypes.c_void_p(FAKE + 0x100000 * 30 + 2)
+    assert bwd(lib, d, ws=40, ws_bytes=need, dC=odd4) == INVALID
+    assert "aligned" in err(lib)
+    # without a gate dz is ignored, so it may alias anything
+    assert bwd(lib, d, ws=None, ws_bytes=0, z=None, dz=1) == INVALID
+    assert "workspace" in err(lib)
+    # nothing to do for dim == 0; dA is required otherwise, even with no steps
+    assert bwd(lib, D_(dim=0), **{k: None for k in BWD_ARGS}) == 0
+    assert bwd(lib, D_(seqlen=0), dA=None) == INVALID
