@@ -8,12 +8,15 @@ synthetic tensors already resident in HBM; the timed region holds exactly
 --steps calls bracketed by device synchronisation.
 
 Prints one JSON line. `value` is elem-steps/s (batch * L * channels per
-second). `roofline` relates the scan kernel's algorithmic HBM bytes per
-launch (every input read once, y and the final state written once) to its
-average launch time measured with HIP events on the launch stream.
-`cpu_baseline` is the fp64 oracle timed on this host on the same workload.
-The decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32 state) is
-measured in the same run and reported under `decode`.
+second). `roofline` relates the scan call's algorithmic fp32 operations to
+the vector-ALU peak (the scan is bound by vector-ALU issue), from its average
+launch time measured with HIP events on the launch stream; `hbm` gives the
+same call's algorithmic HBM bytes (every input read once, y and the final
+state written once) against the HBM peak. `cpu_baseline` is the fp64 oracle
+timed on this host on a bounded sample of the same workload. Measured in the
+same run, each with its own roofline: the backward call on the same layer
+(`bwd`), the decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32
+state, `decode`) and the causal convolution front-end (`conv`).
 """
 from __future__ import annotations
 
@@ -38,6 +41,7 @@ KERNEL_SOURCES = {
     "decode": ["state_update.hip", "device_math.h", "kernels.h"],
     "conv": ["conv1d.hip", "device_math.h", "conv.h"],
     "conv_update": ["conv1d.hip", "device_math.h", "conv.h"],
+    "bwd": ["scan_bwd.hip", "scan_fwd.hip", "tile_io.h", "device_math.h", "kernels.h"],
 }
 
 
@@ -86,6 +90,35 @@ def scan_flops(w) -> int:
     multiply) and the gate multiply (5)."""
     per_row_step = 7 * w.dstate + 7 + (5 if w.gate else 0)
     return w.batch * w.seqlen * w.dim * per_row_step
+
+
+def bwd_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: x, Delta_raw, z and dy read
+    and dx, dDelta_raw, dz written (io dtype, once per element), B and C read
+    and the fp32 dB and dC written once per token, A, D and bias read and dA,
+    dD, dbias written once per channel, the fp32 final-state gradient read
+    and the initial-state gradient written once per row."""
+    eb = 2 if w.io == "bf16" else 4
+    elems = w.batch * w.seqlen * w.dim
+    io_in = 4 if w.gate else 3
+    io_out = 3 if w.gate else 2
+    tok = w.batch * w.seqlen * w.dstate
+    rows = w.batch * w.dim * w.dstate
+    return (elems * eb * (io_in + io_out) + tok * (2 * eb + 2 * 4) + 2 * (w.dim * w.dstate * 4 + 2 * w.dim * 4)
+            + 2 * rows * 4)
+
+
+def bwd_flops(w) -> int:
+    """Algorithmic fp32 operations of one backward call (an FMA counts as 2,
+    a transcendental as 1), the recomputation of the states included (the
+    method recomputes rather than stores them). Per (step, state): decay
+    Delta*A and exp (2), state Delta*x*B and FMA (3), adjoint C*ds + (2),
+    abar*h_{t-1}*lam (2), dA, A-term of dDelta, lam*B, C*h read-out FMAs (8),
+    dB and dC products and their sums over channels (4), abar*lam (1) = 22.
+    Per (step, channel): softplus (3), sigmoid of the Delta input (3),
+    silu(z) and its sigmoid (4), ds (1), dx (3), dDelta_raw (3), dz (5), the
+    dD and dbias sums (3) = 25."""
+    return w.batch * w.seqlen * w.dim * (22 * w.dstate + 25)
 
 
 def decode_bytes(w) -> int:
@@ -186,6 +219,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -273,6 +307,40 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
                 "achieved_at_median": nbytes / (call_stats(per_call)["median_launch_ms"] * 1e-3) / 1e9},
     }
+
+    if not args.no_bwd:
+        from selective_state_space_56_amd import scan_bwd
+        from selective_state_space_56_amd.workloads import make_bwd_grads
+        gr = make_bwd_grads(w, device=dev)
+
+        def bstep():
+            scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], gr["dout"], D=inp["D"],
+                     z=inp["z"], delta_bias=inp["delta_bias"], dlast=gr["dlast"])
+
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        nb = max(5, args.steps // 5)
+        bcalls = time_calls(bstep, nb, stream)
+        bms = sum(bcalls) / len(bcalls)
+        bfl = bwd_flops(w)
+        bby = bwd_bytes(w)
+        rec["bwd"] = {
+            "op": "mamba_scan_bwd (all gradients, states recomputed)", "workload": w.name,
+            "calls": nb, "avg_launch_ms": bms, **call_stats(bcalls),
+            "value": w.elem_steps / (bms * 1e-3), "unit": "elem-steps/s",
+            "roofline": {"bound": "alu", "achieved": bfl / (bms * 1e-3) / 1e12,
+                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": bfl / (bms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+                         "traffic": recorded_traffic("bwd", w.name),
+                         "algorithmic_flops_per_launch": bfl},
+            "hbm": {"achieved": bby / (bms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes_per_launch": bby},
+            "workspace_bytes": binding.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
+                                                          w.torch_io),
+        }
+        del gr
 
     if not args.no_decode:
         wd = WORKLOADS["decode_4096"]
