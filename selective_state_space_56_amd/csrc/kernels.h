@@ -41,11 +41,12 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
 hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* workspace,
                            hipStream_t stream);
 
-// The first two launches of launch_scan_fwd alone (out and last_state are not
-// touched). Afterwards, in stream order, the workspace starts with the state
-// entering every segment s >= 1: float[segments - 1][batch * dim][dstate], slot
-// s - 1 for segment s (nothing when plan.segments < 2).
-hipError_t launch_scan_carries(const ScanProblem& p, const ScanPlan& plan, void* workspace,
+// The combine launch of launch_scan_fwd on its own: folds segment
+// aggregates ws_h[k][rows][dstate] (end state from zero) and ws_s[k][rows]
+// (sum of Delta), k < segments - 1, from h0 (or zero) in time order, leaving
+// the state that enters segment k + 1 in slot k.
+hipError_t launch_scan_combine(const float* A, float* ws_h, const float* ws_s, const float* h0,
+                               int64_t rows, int64_t dim, int dstate, int segments,
                                hipStream_t stream);
 
 // Compute units of the current HIP device (256 when it cannot be queried).
@@ -81,11 +82,11 @@ struct ScanBwdProblem {
   int io;
 };
 
-// Segmentation (shared with the forward carries, whose workspace comes first)
-// and byte offsets of the backward's workspace regions.
+// Time segmentation and byte offsets of the backward's workspace regions
+// (the forward carries come first).
 struct ScanBwdPlan {
   ScanPlan seg;
-  size_t adj_off, ck_off, pa_off, pdb_off, pbc_off;
+  size_t adj_off, ck_off, cks_off, pa_off, pdb_off, pbc_off;
   size_t workspace_bytes;
 };
 

@@ -23,7 +23,9 @@
 //   dh0      = abar_0 lam_0
 //
 // Time is cut into segments as in the forward scan. Launches, in order:
-//   F. the forward scan's aggregate and combine: every segment's carry-in state;
+//   0. state checkpoints: every segment scans forward from zero and stores its
+//      state and Delta sum at every chunk start, and its end state; the
+//      forward scan's combine turns the end states into carry-in states;
 //   1. adjoint aggregate: every segment but the first runs the adjoint
 //      recurrence backwards from zero and records abar at its first step times
 //      the adjoint there, and its sum of Delta;
@@ -31,10 +33,9 @@
 //      gives the adjoint that enters each segment from later time (the affine
 //      pair combine of the forward scan run backwards: over a segment the
 //      adjoint decays by exp(A_n sum Delta));
-//   3. main: each segment scans forward from its carry-in and stores the state
-//      at the start of every chunk of kChunk steps (checkpoints, in the
-//      workspace), then walks its chunks backwards: it recomputes the chunk's
-//      states from the checkpoint into registers and steps the adjoint back
+//   3. main: each segment walks its chunks of kChunk steps backwards: it
+//      forms the state before the chunk from the checkpoint and the carry-in,
+//      recomputes the chunk's states into registers and steps the adjoint back
 //      through them, writing dx, dDelta_raw and dz and accumulating dA, dD and
 //      dbias per lane; dB and dC of a step are summed over the wave's channels
 //      with cross-lane exchanges, then over the workgroup's waves in LDS, and
@@ -55,10 +56,13 @@ struct BwdDims {
   unsigned tiles;
 };
 
-// Pointers of one backward call. carry_h: forward carry-in states (slot s - 1
-// for segment s); carry_a: adjoint aggregates, then (after the fold) the
-// adjoint entering segment s from later time in slot s; ck: checkpoints; pA,
-// pDb, pBC: partial sums.
+// Pointers of one backward call. carry_h / carry_hs: the end state from zero
+// and the Delta sum of segment k in slot k, then (after the forward combine)
+// the state entering segment s in slot s - 1; carry_a / carry_s: adjoint
+// aggregates, then (after the fold) the adjoint entering segment s from later
+// time in slot s; ck / ck_s: per chunk, the state before its first step from
+// the segment's start from zero, and the Delta sum from the segment's start;
+// pA, pDb, pBC: partial sums.
 struct BwdPtrs {
   const void* x;
   const void* delta;
@@ -75,16 +79,33 @@ struct BwdPtrs {
   void* ddelta;
   void* dz;
   float* dh0;
-  const float* carry_h;
+  float* carry_h;  // segment end states from zero, then (after the combine) carry-in states
+  float* carry_hs;  // segment sums of Delta
   float* carry_a;
   float* carry_s;
   float* ck;
+  float* ck_s;
   float* pA;
   float* pDb;
   float* pBC;
 };
 
+// |Delta x| floor of the rescaled form (the forward scan's value).
+constexpr float kDxFloorBwd = 1e-20f;
+
 __device__ __forceinline__ float sigmoid_f(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// The value of lane l ^ 2^K: quad permutes (DPP) for K = 0, 1, otherwise a
+// cross-lane read through the LDS crossbar.
+template <int K>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (K == 0)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+  else if constexpr (K == 1)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+  else
+    return __shfl_xor(v, 1 << K);
+}
 
 template <int M>
 constexpr int log2_of() {
@@ -93,13 +114,21 @@ constexpr int log2_of() {
   return k;
 }
 
-// Sums M values (M a power of two, at most 64) over the 64 lanes of a wave by
-// recursive halving: at level k, lane l keeps one half of its values, sends
-// the other half to lane l ^ 2^k and adds what that lane sends back. Lane l
-// ends with the wave total of value scatter_index<M>(l). Each level is its own
-// instantiation so that every array index is a compile-time constant.
-// sum_scatter_level<W, K>: the levels from lane bit K on, for the W values
-// v[0 .. W) left at that point.
+// Channel sums of dB and dC within a wave. Every lane holds, per step, N dB
+// terms and N dC terms; the wave's 64 lanes are summed by recursive halving,
+// each level leaving half of the values on each lane of a pair, so that at
+// the end every value's total sits on some lane:
+//   level 0, lane bit 5: v_permlane32_swap exchanges the upper half-wave of
+//     the dB term with the lower half-wave of the dC term (per state, inline
+//     in the step); the sum of the two results is the dB total over the lane
+//     pair on lanes 0-31 and the dC total on lanes 32-63;
+//   level 1, lane bit 4: v_permlane16_swap does the same between rows of 16
+//     lanes for states n and n + N/2;
+//   then, lane bits 0, 1, 2: lane l keeps one half of its values and adds the
+//     other half of lane l ^ 2^k's (selected per lane);
+//   the remaining lane bits add the one value left.
+// The swap levels need no per-lane selection; they act where the most values
+// are left.
 template <int W, int K, int SZ>
 __device__ __forceinline__ void sum_scatter_level(float (&v)[SZ], int lane) {
   if constexpr (W >= 2) {
@@ -109,34 +138,56 @@ __device__ __forceinline__ void sum_scatter_level(float (&v)[SZ], int lane) {
     for (int i = 0; i < H; ++i) {
       const float keep = hi ? v[i + H] : v[i];
       const float send = hi ? v[i] : v[i + H];
-      v[i] = keep + __shfl_xor(send, 1 << K);
+      v[i] = keep + lane_xor<K>(send);
     }
     sum_scatter_level<H, K + 1>(v, lane);
   }
 }
 
-// The remaining levels once one value is left (lane bits K .. 5).
-template <int K>
-__device__ __forceinline__ float wave_sum_rest(float r) {
-#pragma unroll
-  for (int k = K; k < 6; ++k) r += __shfl_xor(r, 1 << k);
-  return r;
-}
+template <int N>
+struct BcReduce {
+  static constexpr int kW = N >= 2 ? N / 2 : 1;  // values left after the swap levels
+  static constexpr int kSel = log2_of<kW>();     // select levels, lane bits 0 .. kSel - 1
+  // lane bits summed at the end: kSel .. 3, and 4 when N == 1
+  static constexpr int kRestMask = (0xf & ~((1 << kSel) - 1)) | (N == 1 ? 0x10 : 0);
 
-template <int M>
-__device__ __forceinline__ float wave_sum_scatter(float (&v)[M], int lane) {
-  sum_scatter_level<M, 0>(v, lane);
-  return wave_sum_rest<log2_of<M>()>(v[0]);
-}
-
-template <int M>
-__device__ __forceinline__ int scatter_index(int lane) {
-  constexpr int kLevels = log2_of<M>();
-  int e = 0;
+  // value index (n for dB_n, N + n for dC_n) whose wave total lane ends with
+  static __device__ __forceinline__ int index(int lane) {
+    int e = ((lane >> 5) & 1) * N;
+    if (N >= 2) e += ((lane >> 4) & 1) * (N / 2);
 #pragma unroll
-  for (int k = 0; k < kLevels; ++k) e += ((lane >> k) & 1) * (M >> (k + 1));
-  return e;
-}
+    for (int k = 0; k < kSel; ++k) e += ((lane >> k) & 1) * (kW >> (k + 1));
+    return e;
+  }
+  // one lane per value stores its total
+  static __device__ __forceinline__ bool writer(int lane) { return (lane & kRestMask) == 0; }
+
+  // level 0 for one state: the dB and dC terms of state n
+  static __device__ __forceinline__ float level0(float db, float dc) {
+    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(db), __float_as_uint(dc), false,
+                                                    false);
+    return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+  }
+  // the remaining levels on the N level-0 results
+  static __device__ __forceinline__ float rest(float (&t)[N], int lane) {
+    if constexpr (N >= 2) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[i]),
+                                                        __float_as_uint(t[i + N / 2]), false, false);
+        t[i] = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+      }
+    }
+    sum_scatter_level<kW, 0>(t, lane);
+    float r = t[0];
+    if constexpr ((kRestMask & 1) != 0) r += lane_xor<0>(r);
+    if constexpr ((kRestMask & 2) != 0) r += lane_xor<1>(r);
+    if constexpr ((kRestMask & 4) != 0) r += lane_xor<2>(r);
+    if constexpr ((kRestMask & 8) != 0) r += lane_xor<3>(r);
+    if constexpr ((kRestMask & 16) != 0) r += lane_xor<4>(r);
+    return r;
+  }
+};
 
 // LDS staging of one chunk: NIN input tiles (raw io values), the chunk's B and
 // C widened to fp32, NOUT output tiles and the per-wave dB/dC sums (double
@@ -285,6 +336,138 @@ __device__ __forceinline__ bool tile_is_structured(const float* A, int64_t d) {
   return __syncthreads_and(structured);
 }
 
+// Checkpoint layout: float[chunk][N / 4][rows][4] (N >= 4) or
+// float[chunk][N][rows]: the state before the chunk's first step, for every
+// chunk of kChunk steps of the sequence.
+template <int N>
+__device__ __forceinline__ void ck_store(float* ck, int64_t chunk, int64_t rows, int64_t row,
+                                         const float (&v)[N]) {
+  float* base = ck + chunk * rows * N;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      *reinterpret_cast<float4*>(base + (q * rows + row) * 4) =
+          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) base[n * rows + row] = v[n];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void ck_load(const float* ck, int64_t chunk, int64_t rows, int64_t row,
+                                        float (&v)[N]) {
+  const float* base = ck + chunk * rows * N;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 w = *reinterpret_cast<const float4*>(base + (q * rows + row) * 4);
+      v[4 * q] = w.x;
+      v[4 * q + 1] = w.y;
+      v[4 * q + 2] = w.z;
+      v[4 * q + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = base[n * rows + row];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 0. State checkpoints. Grid: x = batch * channel tiles, y = segment. Scans
+// segment blockIdx.y forward from zero; at the start of every chunk it stores
+// the state and the Delta sum so far (the state there is this local state
+// plus exp(A * Delta sum) times the segment's carry-in state: the affine-pair
+// combine); every segment but the last also stores its end state and Delta
+// sum for the forward combine. S4D-Real-shaped tiles run the rescaled form of
+// the forward scan (g = h / (Delta x) and one exponential per step, with
+// Delta x kept away from zero by at most 1e-20).
+template <class IO>
+constexpr int kCkBlocksPerCU = sizeof(typename IO::raw) == 2 ? 5 : 3;
+
+template <int N, class IO, int CW, bool STRUCT>
+__global__ __launch_bounds__(kBlock, kCkBlocksPerCU<IO>) void bwd_state_checkpoint_kernel(BwdPtrs a, BwdDims g) {
+  using raw = typename IO::raw;
+  __shared__ BwdStage<N, IO, 2, 0> st;  // x, Delta_raw
+  const int tid = threadIdx.x;
+  const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y);
+  if (tile_is_structured<N>(a.A, tc.d) != STRUCT) return;
+  float A2[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) A2[n] = a.A[tc.d * N + n] * kLog2e;
+  const float bias = a.bias ? a.bias[tc.d] : 0.0f;
+  const raw* const src[2] = {static_cast<const raw*>(a.x) + tc.row0,
+                             static_cast<const raw*>(a.delta) + tc.row0};
+  TileRegs<IO> regs[2];
+  float bcv[TileCtx<N, IO, CW>::kBcPer];
+  const int last = static_cast<int>((tc.steps + kChunk - 1) / kChunk) - 1;
+  const int64_t ck0 = tc.t_begin / kChunk;
+
+  float h[N];  // h, or g = h / dx_prev on structured tiles
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  float dx_prev = 1.0f;
+  float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta
+  tc.fetch(src, 2, 0, &st.in[0][0][0][0], regs);
+  tc.fetch_bc(0, bcv);
+  tc.land(2, &st.in[0][0][0][0], regs);
+  tc.land_bc(bcv, st.bc[0]);
+  wait_vmem();
+  __syncthreads();
+  for (int c = 0; c <= last; ++c) {
+    const int buf = c & 1;
+    if (c < last) {
+      tc.fetch(src, 2, (c + 1) * kChunk, &st.in[buf ^ 1][0][0][0], regs);
+      tc.fetch_bc((c + 1) * kChunk, bcv);
+    }
+    if (tc.active) {
+      float hv[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) hv[n] = STRUCT ? h[n] * dx_prev : h[n];
+      ck_store<N>(a.ck, ck0 + c, g.rows, tc.row, hv);
+      a.ck_s[(ck0 + c) * g.rows + tc.row] = S;
+    }
+    const int valid = static_cast<int>(tc.steps) - c * kChunk;
+    float dsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (j < valid) {
+        const float xf = IO::to_f32(st.in[buf][0][j][tid]);
+        const float Delta = softplus_f(IO::to_f32(st.in[buf][1][j][tid]) + bias);
+        const float* Br = &st.bc[buf][j][0];
+        if constexpr (STRUCT) {
+          const float dx = fmaf(Delta, xf, copysignf(kDxFloorBwd, xf));
+          float p[N];
+          scaled_powers<N>(hw_exp2(Delta * A2[0]), dx_prev * hw_rcp(dx), p);
+          dx_prev = dx;
+#pragma unroll
+          for (int n = 0; n < N; ++n) h[n] = fmaf(p[n], h[n], Br[n]);
+        } else {
+          const float dxv = Delta * xf;
+#pragma unroll
+          for (int n = 0; n < N; ++n) h[n] = fmaf(hw_exp2(Delta * A2[n]), h[n], dxv * Br[n]);
+        }
+        dsum += Delta;
+      }
+    }
+    const float v = dsum - S_c;
+    const float tsum = S + v;
+    S_c = (tsum - S) - v;
+    S = tsum;
+    if (c < last) {
+      tc.land(2, &st.in[buf ^ 1][0][0][0], regs);
+      tc.land_bc(bcv, st.bc[buf ^ 1]);
+      wait_vmem();
+    }
+    __syncthreads();
+  }
+  if (!tc.active || tc.s + 1 >= g.segments) return;
+  const int64_t slot = static_cast<int64_t>(tc.s) * g.rows + tc.row;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.carry_h[slot * N + n] = STRUCT ? h[n] * dx_prev : h[n];
+  a.carry_hs[slot] = S;
+}
+
 // ---------------------------------------------------------------------------
 // 1. Adjoint aggregate. Grid: x = batch * channel tiles, y = segment - 1.
 // Runs the adjoint recurrence of segment blockIdx.y + 1 backwards from zero;
@@ -406,43 +589,6 @@ __global__ __launch_bounds__(kAuxBlock) void bwd_adjoint_fold_kernel(const float
 
 // ---------------------------------------------------------------------------
 // 3. Main pass. Grid: x = batch * channel tiles, y = segment.
-// Checkpoint layout: float[chunk][N / 4][rows][4] (N >= 4) or
-// float[chunk][N][rows]: the state before the chunk's first step, for every
-// chunk of kChunk steps of the sequence.
-template <int N>
-__device__ __forceinline__ void ck_store(float* ck, int64_t chunk, int64_t rows, int64_t row,
-                                         const float (&v)[N]) {
-  float* base = ck + chunk * rows * N;
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q)
-      *reinterpret_cast<float4*>(base + (q * rows + row) * 4) =
-          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-  } else {
-#pragma unroll
-    for (int n = 0; n < N; ++n) base[n * rows + row] = v[n];
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void ck_load(const float* ck, int64_t chunk, int64_t rows, int64_t row,
-                                        float (&v)[N]) {
-  const float* base = ck + chunk * rows * N;
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      const float4 w = *reinterpret_cast<const float4*>(base + (q * rows + row) * 4);
-      v[4 * q] = w.x;
-      v[4 * q + 1] = w.y;
-      v[4 * q + 2] = w.z;
-      v[4 * q + 3] = w.w;
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < N; ++n) v[n] = base[n * rows + row];
-  }
-}
-
 // STRUCT: the launch for S4D-Real-shaped channel tiles (the others leave at
 // once), or for the general ones.
 template <int N, class IO, bool GATE, int CW, bool STRUCT>
@@ -493,50 +639,9 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
   const int last = static_cast<int>((tc.steps + kChunk - 1) / kChunk) - 1;
   const int64_t ck0 = tc.t_begin / kChunk;  // sequence chunk index of the segment's chunk 0
 
-  // Forward sweep from the carry-in: checkpoint at every chunk start.
-  {
-    float h[N];
-    if (s > 0) {
-      const float* hin = a.carry_h + (static_cast<int64_t>(s - 1) * g.rows + tc.row) * N;
-#pragma unroll
-      for (int n = 0; n < N; ++n) h[n] = hin[n];
-    } else {
-#pragma unroll
-      for (int n = 0; n < N; ++n) h[n] = a.h0 ? a.h0[tc.row * N + n] : 0.0f;
-    }
-    tc.fetch(src, 2, 0, &st.in[0][0][0][0], regs);
-    tc.fetch_bc(0, bcv);
-    tc.land(2, &st.in[0][0][0][0], regs);
-    tc.land_bc(bcv, st.bc[0]);
-    wait_vmem();
-    __syncthreads();
-    for (int c = 0; c <= last; ++c) {
-      const int buf = c & 1;
-      if (c < last) {
-        tc.fetch(src, 2, (c + 1) * kChunk, &st.in[buf ^ 1][0][0][0], regs);
-        tc.fetch_bc((c + 1) * kChunk, bcv);
-      }
-      if (active) ck_store<N>(a.ck, ck0 + c, g.rows, tc.row, h);
-      const int valid = static_cast<int>(tc.steps) - c * kChunk;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        if (j < valid) {
-          const float Delta = softplus_f(u_at(buf, j));
-          const float dxv = Delta * x_at(buf, j);
-          const float* Br = &st.bc[buf][j][0];
-          Decays<N, STRUCT> ab(Delta, A2);
-#pragma unroll
-          for (int n = 0; n < N; ++n) h[n] = fmaf(ab.next(n, A2), h[n], dxv * Br[n]);
-        }
-      }
-      if (c < last) {
-        tc.land(2, &st.in[buf ^ 1][0][0][0], regs);
-        tc.land_bc(bcv, st.bc[buf ^ 1]);
-        wait_vmem();
-      }
-      __syncthreads();
-    }
-  }
+  // carry-in state of the segment (null: zeros)
+  const float* cin = s > 0 ? a.carry_h + (static_cast<int64_t>(s - 1) * g.rows + tc.row) * N
+                           : (a.h0 ? a.h0 + tc.row * N : nullptr);
 
   // Reverse sweep over the chunks.
   float m[N];  // abar_{t+1} lam_{t+1}: the adjoint entering from later time
@@ -552,8 +657,8 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
 #pragma unroll
   for (int n = 0; n < N; ++n) dA[n] = 0.0f;
   float dD = 0.0f, dbias = 0.0f;
-  const int e_idx = scatter_index<M>(lane);
-  const bool hi0 = lane & 1;
+  const int e_idx = BcReduce<N>::index(lane);
+  const bool bc_writer = BcReduce<N>::writer(lane);
   float* pbc = a.pBC + ((static_cast<int64_t>(tc.tile) * g.batch + tc.b) * g.seqlen + tc.t_begin) * M;
 
   {
@@ -580,6 +685,12 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
       float hc[N];
       if (active) {
         ck_load<N>(a.ck, ck0 + c, g.rows, tc.row, hc);
+        if (cin) {
+          // plus the carry-in decayed over the segment's steps before the chunk
+          Decays<N, STRUCT> dk(a.ck_s[(ck0 + c) * g.rows + tc.row], A2);
+#pragma unroll
+          for (int n = 0; n < N; ++n) hc[n] = fmaf(dk.next(n, A2), cin[n], hc[n]);
+        }
       } else {
 #pragma unroll
         for (int n = 0; n < N; ++n) hc[n] = 0.0f;
@@ -619,7 +730,7 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
         read_bc<N>(st.bc[buf][j], bc, true);
         Decays<N, STRUCT> ab(Delta, A2);
         float sAq = 0.0f, sLB = 0.0f, ypre = Dd * xf;
-        float r[N];  // dB / dC of this step after the first halving level
+        float r[N];  // dB / dC terms of this step after the first halving level
 #pragma unroll
         for (int n = 0; n < N; ++n) {
           const float lam = fmaf(bc[N + n], ds, m[n]);
@@ -629,15 +740,12 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
           sAq = fmaf(STRUCT ? static_cast<float>(n + 1) : A2[n], q, sAq);
           sLB = fmaf(lam, bc[n], sLB);
           ypre = fmaf(bc[N + n], hist[j][n], ypre);
-          const float vb = lam * dxv, vc = ds * hist[j][n];
-          const float keep = hi0 ? vc : vb, send = hi0 ? vb : vc;
-          r[n] = keep + __shfl_xor(send, 1);
+          r[n] = BcReduce<N>::level0(lam * dxv, ds * hist[j][n]);
           m[n] = ab.next(n, A2) * lam;
         }
         if (STRUCT) sAq *= A2[0];
-        sum_scatter_level<N, 1>(r, lane);
-        const float tot = wave_sum_rest<log2_of<M>()>(r[0]);
-        if (lane < M) st.red[tc.wv][j][e_idx] = tot;
+        const float tot = BcReduce<N>::rest(r, lane);
+        if (bc_writer) st.red[tc.wv][j][e_idx] = tot;
         const float dDelta = fmaf(sAq, kLn2, xf * sLB);
         const float ddr = dDelta * sigmoid_f(u);
         dbias += ddr;
@@ -765,34 +873,24 @@ hipError_t launch_typed(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* 
   a.ddelta = p.ddelta;
   a.dz = p.dz;
   a.dh0 = p.dh0;
-  a.carry_h = reinterpret_cast<const float*>(ws);
+  a.carry_h = reinterpret_cast<float*>(ws);
+  a.carry_hs = a.carry_h + static_cast<int64_t>(g.segments > 1 ? g.segments - 1 : 0) * g.rows * N;
   a.carry_a = reinterpret_cast<float*>(ws + plan.adj_off);
   a.carry_s = a.carry_a + static_cast<int64_t>(g.segments > 1 ? g.segments - 1 : 0) * g.rows * N;
   a.ck = reinterpret_cast<float*>(ws + plan.ck_off);
+  a.ck_s = reinterpret_cast<float*>(ws + plan.cks_off);
   a.pA = reinterpret_cast<float*>(ws + plan.pa_off);
   a.pDb = reinterpret_cast<float*>(ws + plan.pdb_off);
   a.pBC = reinterpret_cast<float*>(ws + plan.pbc_off);
 
   const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
+  hipLaunchKernelGGL((bwd_state_checkpoint_kernel<N, IO, CW, true>), dim3(blocks, g.segments),
+                     dim3(kBlock), 0, stream, a, g);
+  hipLaunchKernelGGL((bwd_state_checkpoint_kernel<N, IO, CW, false>), dim3(blocks, g.segments),
+                     dim3(kBlock), 0, stream, a, g);
   if (g.segments > 1) {
-    ScanProblem f;
-    f.x = p.x;
-    f.delta = p.delta;
-    f.A = p.A;
-    f.B = p.B;
-    f.C = p.C;
-    f.D = p.D;
-    f.z = p.z;
-    f.bias = p.bias;
-    f.h0 = p.h0;
-    f.out = nullptr;
-    f.last_state = nullptr;
-    f.batch = p.batch;
-    f.seqlen = p.seqlen;
-    f.dim = p.dim;
-    f.dstate = N;
-    f.io = p.io;
-    hipError_t e = launch_scan_carries(f, plan.seg, ws, stream);
+    hipError_t e = launch_scan_combine(p.A, a.carry_h, a.carry_hs, p.h0, g.rows, p.dim, N,
+                                       g.segments, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_adjoint_aggregate_kernel<N, IO, GATE, CW, true>),
                        dim3(blocks, g.segments - 1), dim3(kBlock), 0, stream, a, g);
@@ -874,11 +972,14 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate
   const size_t R = static_cast<size_t>(rows);
   const size_t tiles = static_cast<size_t>((dim + kBlock - 1) / kBlock);
   const size_t chunks = static_cast<size_t>((seqlen + kChunk - 1) / kChunk);
-  size_t off = round256(plan.seg.workspace_bytes);
+  // segment end states and Delta sums (carries after the combine)
+  size_t off = round256((S - 1) * R * (N + 1) * sizeof(float));
   plan.adj_off = off;
   off += round256((S - 1) * R * (N + 1) * sizeof(float));
   plan.ck_off = off;
   off += round256(chunks * R * N * sizeof(float));
+  plan.cks_off = off;
+  off += round256(chunks * R * sizeof(float));
   plan.pa_off = off;
   off += round256(S * R * N * sizeof(float));
   plan.pdb_off = off;

@@ -471,10 +471,9 @@ __global__ __launch_bounds__(kAuxBlock) void init_state_kernel(float* dst, const
   if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
-// With carries_only, only the aggregate and combine launches run.
 template <int N, class IO, int CW>
 hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* workspace,
-                        hipStream_t stream, bool carries_only) {
+                        hipStream_t stream) {
   using raw = typename IO::raw;
   Dims g;
   g.seqlen = p.seqlen;
@@ -515,7 +514,6 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
     hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s,
                        p.h0, g.rows, p.dim, plan.segments);
   }
-  if (carries_only) return hipGetLastError();
   const dim3 grid(blocks, plan.segments);
   if (z) {
     hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, kFirst>), grid, block, 0,
@@ -540,26 +538,25 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
 // S-byte aligned; otherwise the register-staged copy is used.
 template <int N, class IO>
 hipError_t launch_copy_width(const ScanProblem& p, const ScanPlan& plan, void* ws,
-                             hipStream_t st, bool carries_only) {
+                             hipStream_t st) {
   constexpr int eb = sizeof(typename IO::raw);
   const auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   const auto a4 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 4 == 0; };
   if ((p.dim * eb) % 16 == 0 && a16(p.x) && a16(p.delta) && (!p.z || a16(p.z)))
-    return launch_typed<N, IO, 16>(p, plan, ws, st, carries_only);
+    return launch_typed<N, IO, 16>(p, plan, ws, st);
   if ((p.dim * eb) % 4 == 0 && a4(p.x) && a4(p.delta) && (!p.z || a4(p.z)))
-    return launch_typed<N, IO, 4>(p, plan, ws, st, carries_only);
-  return launch_typed<N, IO, 0>(p, plan, ws, st, carries_only);
+    return launch_typed<N, IO, 4>(p, plan, ws, st);
+  return launch_typed<N, IO, 0>(p, plan, ws, st);
 }
 
 template <class IO>
-hipError_t dispatch_n(const ScanProblem& p, const ScanPlan& plan, void* ws, hipStream_t st,
-                      bool carries_only) {
+hipError_t dispatch_n(const ScanProblem& p, const ScanPlan& plan, void* ws, hipStream_t st) {
   switch (p.dstate) {
-    case 1: return launch_copy_width<1, IO>(p, plan, ws, st, carries_only);
-    case 2: return launch_copy_width<2, IO>(p, plan, ws, st, carries_only);
-    case 4: return launch_copy_width<4, IO>(p, plan, ws, st, carries_only);
-    case 8: return launch_copy_width<8, IO>(p, plan, ws, st, carries_only);
-    case 16: return launch_copy_width<16, IO>(p, plan, ws, st, carries_only);
+    case 1: return launch_copy_width<1, IO>(p, plan, ws, st);
+    case 2: return launch_copy_width<2, IO>(p, plan, ws, st);
+    case 4: return launch_copy_width<4, IO>(p, plan, ws, st);
+    case 8: return launch_copy_width<8, IO>(p, plan, ws, st);
+    case 16: return launch_copy_width<16, IO>(p, plan, ws, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -638,15 +635,25 @@ hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* wor
     }
     return hipSuccess;
   }
-  if (p.io == kIoBf16) return dispatch_n<Bf16Io>(p, plan, workspace, stream, false);
-  return dispatch_n<F32Io>(p, plan, workspace, stream, false);
+  if (p.io == kIoBf16) return dispatch_n<Bf16Io>(p, plan, workspace, stream);
+  return dispatch_n<F32Io>(p, plan, workspace, stream);
 }
 
-hipError_t launch_scan_carries(const ScanProblem& p, const ScanPlan& plan, void* workspace,
+hipError_t launch_scan_combine(const float* A, float* ws_h, const float* ws_s, const float* h0,
+                               int64_t rows, int64_t dim, int dstate, int segments,
                                hipStream_t stream) {
-  if (p.batch == 0 || p.dim == 0 || p.seqlen == 0 || plan.segments < 2) return hipSuccess;
-  if (p.io == kIoBf16) return dispatch_n<Bf16Io>(p, plan, workspace, stream, true);
-  return dispatch_n<F32Io>(p, plan, workspace, stream, true);
+  if (rows == 0 || segments < 2) return hipSuccess;
+  const int64_t work = rows * dstate;
+  const dim3 grid(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock));
+  switch (dstate) {
+    case 1: hipLaunchKernelGGL((scan_combine_kernel<1>), grid, dim3(kAuxBlock), 0, stream, A, ws_h, ws_s, h0, rows, dim, segments); break;
+    case 2: hipLaunchKernelGGL((scan_combine_kernel<2>), grid, dim3(kAuxBlock), 0, stream, A, ws_h, ws_s, h0, rows, dim, segments); break;
+    case 4: hipLaunchKernelGGL((scan_combine_kernel<4>), grid, dim3(kAuxBlock), 0, stream, A, ws_h, ws_s, h0, rows, dim, segments); break;
+    case 8: hipLaunchKernelGGL((scan_combine_kernel<8>), grid, dim3(kAuxBlock), 0, stream, A, ws_h, ws_s, h0, rows, dim, segments); break;
+    case 16: hipLaunchKernelGGL((scan_combine_kernel<16>), grid, dim3(kAuxBlock), 0, stream, A, ws_h, ws_s, h0, rows, dim, segments); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mscan
