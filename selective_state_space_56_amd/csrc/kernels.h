@@ -86,7 +86,7 @@ struct ScanBwdProblem {
 // (the forward carries come first).
 struct ScanBwdPlan {
   ScanPlan seg;
-  size_t adj_off, ck_off, cks_off, pa_off, pdb_off, pbc_off;
+  size_t adj_off, ck_off, cks_off, pa_off, pdb_off, pbc_off, flags_off;
   size_t workspace_bytes;
 };
 

@@ -88,6 +88,7 @@ struct BwdPtrs {
   float* pA;
   float* pDb;
   float* pBC;
+  uint32_t* tile_flags;  // per channel tile: 1 = S4D-Real shaped
 };
 
 // |Delta x| floor of the rescaled form (the forward scan's value).
@@ -336,6 +337,20 @@ __device__ __forceinline__ bool tile_is_structured(const float* A, int64_t d) {
   return __syncthreads_and(structured);
 }
 
+// The decay path of a tile: the first launch of a call classifies the tile
+// and the copy in batch row 0, segment 0 records it; later launches read it.
+template <int N, bool CLASSIFY>
+__device__ __forceinline__ bool tile_path(uint32_t* flags, const float* A, int64_t d, int64_t b,
+                                          int s, unsigned tile) {
+  if constexpr (CLASSIFY) {
+    const bool structured = tile_is_structured<N>(A, d);
+    if (b == 0 && s == 0 && threadIdx.x == 0) flags[tile] = structured ? 1u : 0u;
+    return structured;
+  } else {
+    return flags[tile] != 0u;
+  }
+}
+
 // Checkpoint layout: float[chunk][N / 4][rows][4] (N >= 4) or
 // float[chunk][N][rows]: the state before the chunk's first step, for every
 // chunk of kChunk steps of the sequence.
@@ -391,7 +406,8 @@ __global__ __launch_bounds__(kBlock, kCkBlocksPerCU<IO>) void bwd_state_checkpoi
   __shared__ BwdStage<N, IO, 2, 0> st;  // x, Delta_raw
   const int tid = threadIdx.x;
   const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y);
-  if (tile_is_structured<N>(a.A, tc.d) != STRUCT) return;
+  // the structured launch runs first and classifies the tiles
+  if (tile_path<N, STRUCT>(a.tile_flags, a.A, tc.d, tc.b, tc.s, tc.tile) != STRUCT) return;
   float A2[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) A2[n] = a.A[tc.d * N + n] * kLog2e;
@@ -482,7 +498,7 @@ __global__ __launch_bounds__(kBlock, kAggBlocksPerCU<IO>) void bwd_adjoint_aggre
   __shared__ BwdStage<N, IO, kIn, 0> st;
   const int tid = threadIdx.x;
   const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y + 1);
-  if (tile_is_structured<N>(a.A, tc.d) != STRUCT) return;
+  if (tile_path<N, false>(a.tile_flags, a.A, tc.d, tc.b, tc.s, tc.tile) != STRUCT) return;
 
   float A2[N];
 #pragma unroll
@@ -602,7 +618,7 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const TileCtx<N, IO, CW> tc(g, a.B, a.C, blockIdx.y);
-  if (tile_is_structured<N>(a.A, tc.d) != STRUCT) return;
+  if (tile_path<N, false>(a.tile_flags, a.A, tc.d, tc.b, tc.s, tc.tile) != STRUCT) return;
   const int s = tc.s;
   const bool active = tc.active;
 
@@ -685,15 +701,16 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
       float hc[N];
       if (active) {
         ck_load<N>(a.ck, ck0 + c, g.rows, tc.row, hc);
-        if (cin) {
-          // plus the carry-in decayed over the segment's steps before the chunk
-          Decays<N, STRUCT> dk(a.ck_s[(ck0 + c) * g.rows + tc.row], A2);
-#pragma unroll
-          for (int n = 0; n < N; ++n) hc[n] = fmaf(dk.next(n, A2), cin[n], hc[n]);
-        }
       } else {
 #pragma unroll
         for (int n = 0; n < N; ++n) hc[n] = 0.0f;
+      }
+      const float cks = active ? a.ck_s[(ck0 + c) * g.rows + tc.row] : 0.0f;
+      if (active && cin) {
+        // plus the carry-in decayed over the segment's steps before the chunk
+        Decays<N, STRUCT> dk(cks, A2);
+#pragma unroll
+        for (int n = 0; n < N; ++n) hc[n] = fmaf(dk.next(n, A2), cin[n], hc[n]);
       }
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
@@ -786,6 +803,22 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
 
 // ---------------------------------------------------------------------------
 // 4. Sums of the partials.
+// sum_{k < count} p[k * stride] in four interleaved partial sums (their loads
+// in flight together), added in a fixed order.
+__device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_t stride,
+                                            int64_t count) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int64_t k = 0;
+  for (; k + 4 <= count; k += 4) {
+    s0 += p[k * stride];
+    s1 += p[(k + 1) * stride];
+    s2 += p[(k + 2) * stride];
+    s3 += p[(k + 3) * stride];
+  }
+  for (; k < count; ++k) s0 += p[k * stride];
+  return (s0 + s1) + (s2 + s3);
+}
+
 // dA[d, n] = sum_p pA[p, d, n]; dD[d], dbias[d] likewise from pDb[p, 0 / 1, d].
 template <int N>
 __global__ __launch_bounds__(kAuxBlock) void bwd_param_sum_kernel(const float* __restrict__ pA,
@@ -797,17 +830,12 @@ __global__ __launch_bounds__(kAuxBlock) void bwd_param_sum_kernel(const float* _
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
   const int64_t na = dim * N;
   if (i < na) {
-    float acc = 0.0f;
-    for (int64_t p = 0; p < parts; ++p) acc += pA[p * na + i];
-    dA[i] = acc;
+    dA[i] = strided_sum(pA + i, na, parts);
   } else if (i < na + 2 * dim) {
     const int64_t j = i - na;
     const int64_t which = j / dim, d = j % dim;
     float* outp = which == 0 ? dD : dbias;
-    if (!outp) return;
-    float acc = 0.0f;
-    for (int64_t p = 0; p < parts; ++p) acc += pDb[(p * 2 + which) * dim + d];
-    outp[d] = acc;
+    if (outp) outp[d] = strided_sum(pDb + which * dim + d, 2 * dim, parts);
   }
 }
 
@@ -820,8 +848,7 @@ __global__ __launch_bounds__(kAuxBlock) void bwd_bc_sum_kernel(const float* __re
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
   const int64_t total = tokens * 2 * N;
   if (i >= total) return;
-  float acc = 0.0f;
-  for (unsigned k = 0; k < tiles; ++k) acc += pBC[static_cast<int64_t>(k) * total + i];
+  const float acc = strided_sum(pBC + i, total, tiles);
   const int64_t tok = i / (2 * N);
   const int k = static_cast<int>(i % (2 * N));
   if (k < N)
@@ -882,6 +909,7 @@ hipError_t launch_typed(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* 
   a.pA = reinterpret_cast<float*>(ws + plan.pa_off);
   a.pDb = reinterpret_cast<float*>(ws + plan.pdb_off);
   a.pBC = reinterpret_cast<float*>(ws + plan.pbc_off);
+  a.tile_flags = reinterpret_cast<uint32_t*>(ws + plan.flags_off);
 
   const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
   hipLaunchKernelGGL((bwd_state_checkpoint_kernel<N, IO, CW, true>), dim3(blocks, g.segments),
@@ -987,6 +1015,8 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate
   plan.pbc_off = off;
   off += round256(tiles * static_cast<size_t>(batch) * static_cast<size_t>(seqlen) * 2 * N *
                   sizeof(float));
+  plan.flags_off = off;
+  off += round256(tiles * sizeof(uint32_t));
   plan.workspace_bytes = off;
   return plan;
 }
