@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--parts", default="fwd,bwd,decode,conv",
+                    help="comma list of the parts to run (profiling runs take one family at a time); "
+                         "without fwd only the other parts' objects are printed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -246,15 +249,37 @@ def main():
     if not os.path.exists(binding.LIB_PATH):
         from selective_state_space_56_amd.build import build
         build()
-    from selective_state_space_56_amd import scan_fwd, state_update
-    from selective_state_space_56_amd.workloads import (WORKLOADS, make_decode_state,
-                                                        make_decode_token, make_params,
-                                                        make_scan_inputs)
+    from selective_state_space_56_amd import scan_fwd
+    from selective_state_space_56_amd.workloads import WORKLOADS, make_scan_inputs
 
+    parts = set(args.parts.split(","))
+    run_fwd = "fwd" in parts
+    run_bwd = "bwd" in parts and not args.no_bwd
+    run_decode = "decode" in parts and not args.no_decode
+    run_conv = "conv" in parts and not args.no_conv
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
     inp = make_scan_inputs(w, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rec = {}
+    if run_fwd:
+        rec = fwd_part(args, w, inp, stream, scan_fwd, binding)
+    if run_bwd:
+        rec["bwd"] = bwd_part(args, w, inp, stream, binding)
+    if run_decode:
+        rec["decode"] = decode_part(stream)
+    if run_conv:
+        rec["conv"] = conv_part(args, w, stream)
+    if run_fwd and not args.no_cpu_baseline:
+        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        rec["cpu_baseline"] = cpu_baseline(w, inp, nthreads)
+    print(json.dumps(rec), flush=True)
+
+
+def fwd_part(args, w, inp, stream, scan_fwd, binding):
+    import torch
+    dev = inp["x"].device
     out = torch.empty((w.batch, w.seqlen, w.dim), dtype=w.torch_io, device=dev)
     last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
 
@@ -262,7 +287,6 @@ def main():
         scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
                  delta_bias=inp["delta_bias"], out=out, last_state=last, segments=args.segments)
 
-    stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -308,125 +332,136 @@ def main():
                 "achieved_at_median": nbytes / (call_stats(per_call)["median_launch_ms"] * 1e-3) / 1e9},
     }
 
-    if not args.no_bwd:
-        from selective_state_space_56_amd import scan_bwd
-        from selective_state_space_56_amd.workloads import make_bwd_grads
-        gr = make_bwd_grads(w, device=dev)
+    return rec
 
-        def bstep():
-            scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], gr["dout"], D=inp["D"],
-                     z=inp["z"], delta_bias=inp["delta_bias"], dlast=gr["dlast"])
 
-        for _ in range(3):
-            bstep()
-        torch.cuda.synchronize()
-        nb = max(5, args.steps // 5)
-        bcalls = time_calls(bstep, nb, stream)
-        bms = sum(bcalls) / len(bcalls)
-        bfl = bwd_flops(w)
-        bby = bwd_bytes(w)
-        rec["bwd"] = {
-            "op": "mamba_scan_bwd (all gradients, states recomputed)", "workload": w.name,
-            "calls": nb, "avg_launch_ms": bms, **call_stats(bcalls),
-            "value": w.elem_steps / (bms * 1e-3), "unit": "elem-steps/s",
-            "roofline": {"bound": "alu", "achieved": bfl / (bms * 1e-3) / 1e12,
-                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": bfl / (bms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
-                         "traffic": recorded_traffic("bwd", w.name),
-                         "algorithmic_flops_per_launch": bfl},
-            "hbm": {"achieved": bby / (bms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "algorithmic_bytes_per_launch": bby},
-            "workspace_bytes": binding.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
-                                                          w.torch_io),
-        }
-        del gr
+def bwd_part(args, w, inp, stream, binding):
+    import torch
+    from selective_state_space_56_amd import scan_bwd
+    from selective_state_space_56_amd.workloads import make_bwd_grads
+    dev = inp["x"].device
+    gr = make_bwd_grads(w, device=dev)
 
-    if not args.no_decode:
-        wd = WORKLOADS["decode_4096"]
-        params = make_params(wd, device=dev)
-        state = make_decode_state(wd, device=dev)
-        toks = [make_decode_token(wd, s, device=dev) for s in range(wd.decode_steps)]
-        outd = torch.empty((wd.batch, wd.dim), dtype=wd.torch_io, device=dev)
-        it = iter(range(10 ** 9))
+    def bstep():
+        scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], gr["dout"], D=inp["D"],
+                 z=inp["z"], delta_bias=inp["delta_bias"], dlast=gr["dlast"])
 
-        def dstep():
-            t = toks[next(it) % wd.decode_steps]
-            state_update(state, t["x"], t["delta"], params["A"], t["B"], t["C"], D=params["D"],
-                         z=t["z"], delta_bias=params["delta_bias"], out=outd)
+    for _ in range(3):
+        bstep()
+    torch.cuda.synchronize()
+    nb = max(5, args.steps // 5)
+    bcalls = time_calls(bstep, nb, stream)
+    bms = sum(bcalls) / len(bcalls)
+    bfl = bwd_flops(w)
+    bby = bwd_bytes(w)
+    out = {
+        "op": "mamba_scan_bwd (all gradients, states recomputed)", "workload": w.name,
+        "calls": nb, "avg_launch_ms": bms, **call_stats(bcalls),
+        "value": w.elem_steps / (bms * 1e-3), "unit": "elem-steps/s",
+        "roofline": {"bound": "alu", "achieved": bfl / (bms * 1e-3) / 1e12,
+                     "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bfl / (bms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+                     "traffic": recorded_traffic("bwd", w.name),
+                     "algorithmic_flops_per_launch": bfl},
+        "hbm": {"achieved": bby / (bms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes_per_launch": bby},
+        "workspace_bytes": binding.bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
+                                                      w.torch_io),
+    }
+    del gr
+    return out
 
-        for _ in range(4):
-            dstep()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        dcalls = time_calls(dstep, wd.decode_steps, stream)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t1
-        dms = sum(dcalls) / len(dcalls)
-        db = decode_bytes(wd)
-        rec["decode"] = {
-            "workload": wd.name, "steps": wd.decode_steps, "ms_total": dt * 1e3,
-            "value": wd.batch * wd.dim * wd.decode_steps / dt, "unit": "elem-steps/s",
-            "avg_launch_ms": dms, **call_stats(dcalls),
-            "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("decode", wd.name),
-                         "algorithmic_bytes_per_launch": db},
-        }
-        del toks, state
 
-    if not args.no_conv:
-        from selective_state_space_56_amd import conv1d_fwd, conv1d_update
-        from selective_state_space_56_amd.workloads import make_conv_inputs
-        ci = make_conv_inputs(w, 4, device=dev)
-        cout = torch.empty_like(ci["xin"])
-        cst = torch.empty_like(ci["state"])
+def decode_part(stream):
+    import torch
+    from selective_state_space_56_amd import state_update
+    from selective_state_space_56_amd.workloads import (WORKLOADS, make_decode_state,
+                                                        make_decode_token, make_params)
+    dev = torch.device("cuda", 0)
+    wd = WORKLOADS["decode_4096"]
+    params = make_params(wd, device=dev)
+    state = make_decode_state(wd, device=dev)
+    toks = [make_decode_token(wd, s, device=dev) for s in range(wd.decode_steps)]
+    outd = torch.empty((wd.batch, wd.dim), dtype=wd.torch_io, device=dev)
+    it = iter(range(10 ** 9))
 
-        def cstep():
-            conv1d_fwd(ci["xin"], ci["weight"], ci["bias"], ci["state"], out=cout, state_out=cst)
+    def dstep():
+        t = toks[next(it) % wd.decode_steps]
+        state_update(state, t["x"], t["delta"], params["A"], t["B"], t["C"], D=params["D"],
+                     z=t["z"], delta_bias=params["delta_bias"], out=outd)
 
-        for _ in range(args.warmup):
-            cstep()
-        torch.cuda.synchronize()
-        ccalls = time_calls(cstep, args.steps, stream)
-        cms = sum(ccalls) / len(ccalls)
-        cb = conv_bytes(w)
-        rec["conv"] = {
-            "op": "mamba_conv1d_fwd (causal depthwise conv, width 4, + SiLU)", "workload": w.name,
-            "avg_launch_ms": cms, **call_stats(ccalls),
-            "value": w.elem_steps / (cms * 1e-3), "unit": "elem-steps/s",
-            "roofline": {"bound": "hbm", "achieved": cb / (cms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("conv", w.name),
-                         "algorithmic_bytes_per_launch": cb},
-        }
-        wd = WORKLOADS["decode_4096"]
-        cd = make_conv_inputs(wd.with_shape(seqlen=1), 4, device=dev)
-        cstate = cd["state"].clone()
-        cx = cd["xin"][:, 0].contiguous()
-        cdo = torch.empty_like(cx)
-        for _ in range(4):
-            conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo)
-        torch.cuda.synchronize()
-        ucalls = time_calls(lambda: conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo),
-                            wd.decode_steps, stream)
-        ums = sum(ucalls) / len(ucalls)
-        ub = conv_update_bytes(wd)
-        rec["conv"]["decode"] = {
-            "op": "mamba_conv1d_update", "workload": wd.name, "avg_launch_ms": ums,
-            **call_stats(ucalls),
-            "roofline": {"bound": "hbm", "achieved": ub / (ums * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": ub / (ums * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": recorded_traffic("conv_update", wd.name),
-                         "algorithmic_bytes_per_launch": ub},
-        }
-        del ci, cout, cst, cd, cstate
+    for _ in range(4):
+        dstep()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dcalls = time_calls(dstep, wd.decode_steps, stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    dms = sum(dcalls) / len(dcalls)
+    db = decode_bytes(wd)
+    out = {
+        "workload": wd.name, "steps": wd.decode_steps, "ms_total": dt * 1e3,
+        "value": wd.batch * wd.dim * wd.decode_steps / dt, "unit": "elem-steps/s",
+        "avg_launch_ms": dms, **call_stats(dcalls),
+        "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic("decode", wd.name),
+                     "algorithmic_bytes_per_launch": db},
+    }
+    del toks, state
+    return out
 
-    if not args.no_cpu_baseline:
-        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
-        rec["cpu_baseline"] = cpu_baseline(w, inp, nthreads)
 
-    print(json.dumps(rec), flush=True)
+def conv_part(args, w, stream):
+    import torch
+    from selective_state_space_56_amd import conv1d_fwd, conv1d_update
+    from selective_state_space_56_amd.workloads import WORKLOADS, make_conv_inputs
+    dev = torch.device("cuda", 0)
+    ci = make_conv_inputs(w, 4, device=dev)
+    cout = torch.empty_like(ci["xin"])
+    cst = torch.empty_like(ci["state"])
+
+    def cstep():
+        conv1d_fwd(ci["xin"], ci["weight"], ci["bias"], ci["state"], out=cout, state_out=cst)
+
+    for _ in range(args.warmup):
+        cstep()
+    torch.cuda.synchronize()
+    ccalls = time_calls(cstep, args.steps, stream)
+    cms = sum(ccalls) / len(ccalls)
+    cb = conv_bytes(w)
+    out = {
+        "op": "mamba_conv1d_fwd (causal depthwise conv, width 4, + SiLU)", "workload": w.name,
+        "avg_launch_ms": cms, **call_stats(ccalls),
+        "value": w.elem_steps / (cms * 1e-3), "unit": "elem-steps/s",
+        "roofline": {"bound": "hbm", "achieved": cb / (cms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic("conv", w.name),
+                     "algorithmic_bytes_per_launch": cb},
+    }
+    wd = WORKLOADS["decode_4096"]
+    cd = make_conv_inputs(wd.with_shape(seqlen=1), 4, device=dev)
+    cstate = cd["state"].clone()
+    cx = cd["xin"][:, 0].contiguous()
+    cdo = torch.empty_like(cx)
+    for _ in range(4):
+        conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo)
+    torch.cuda.synchronize()
+    ucalls = time_calls(lambda: conv1d_update(cstate, cx, cd["weight"], cd["bias"], out=cdo),
+                        wd.decode_steps, stream)
+    ums = sum(ucalls) / len(ucalls)
+    ub = conv_update_bytes(wd)
+    out["decode"] = {
+        "op": "mamba_conv1d_update", "workload": wd.name, "avg_launch_ms": ums,
+        **call_stats(ucalls),
+        "roofline": {"bound": "hbm", "achieved": ub / (ums * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ub / (ums * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic("conv_update", wd.name),
+                     "algorithmic_bytes_per_launch": ub},
+    }
+    del ci, cout, cst, cd, cstate
+    return out
 
 
 if __name__ == "__main__":
