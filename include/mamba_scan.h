@@ -67,11 +67,24 @@ typedef enum mamba_dtype {
 } mamba_dtype;
 
 /*
+ * Input weight of the discretisation. By default Bbar x = Delta B x, the
+ * first-order form ("Mamba and selective state spaces, from first principles",
+ * section "Discretisation: zero-order hold": the form the reference code
+ * computes). With MAMBA_SCAN_ZOH in desc->flags the exact zero-order hold is
+ * used instead: Bbar_n = (exp(Delta A[d,n]) - 1) / A[d,n] B_n (its limit Delta B_n
+ * where Delta A[d,n] is 0); Abar is exp(Delta A) either way. The ZOH mode runs
+ * the general decay path (an exponential per state and step), so it is slower.
+ */
+#define MAMBA_SCAN_ZOH (1u << 16)
+
+/*
  * Problem sizes. dstate (N) must be 1, 2, 4, 8 or 16.
  * flags: for mamba_scan_fwd, bits 0-15 force the number of time segments the
  * sequence is cut into (0 = the library's choice; results agree to rounding
- * for any value, and the workspace size depends on it); all other bits, and
- * every bit for mamba_state_update, must be 0.
+ * for any value, and the workspace size depends on it); MAMBA_SCAN_ZOH selects
+ * the exact zero-order-hold input weight for mamba_scan_fwd, mamba_scan_fwd_init
+ * and mamba_state_update; all other bits, and bits 0-15 for mamba_state_update,
+ * must be 0.
  */
 typedef struct mamba_scan_desc {
   int64_t batch;   /* >= 0                                         */

@@ -50,9 +50,11 @@ extern "C" {
  * Bytes of device workspace mamba_scan_bwd needs (0 when none). Bits 0-15 of
  * desc->flags force the number of time segments (0 = the library's choice,
  * which depends on the compute-unit count of the current device); other bits
- * must be 0. The workspace holds, among others, one fp32 copy of the state
- * per 8 time steps (about batch * seqlen * dim * dstate / 2 bytes). Returns 0
- * for an invalid descriptor as well.
+ * must be 0 (the backward of the MAMBA_SCAN_ZOH mode is not provided:
+ * mamba_scan_bwd returns MAMBA_ERR_UNSUPPORTED for it). The workspace holds,
+ * among others, one fp32 copy of the state per 8 time steps (about
+ * batch * seqlen * dim * dstate / 2 bytes). Returns 0 for an invalid
+ * descriptor as well.
  */
 size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc *desc);
 

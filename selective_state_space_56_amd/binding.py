@@ -120,8 +120,11 @@ def workspace_size(batch, seqlen, dim, dstate, io_dtype=torch.bfloat16, segments
     return int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
 
 
+ZOH_FLAG = 1 << 16  # MAMBA_SCAN_ZOH
+
+
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out=None,
-             last_state=None, return_last_state=True, segments=0):
+             last_state=None, return_last_state=True, segments=0, zoh=False):
     """Selective scan over full sequences.
 
     x, delta (Delta_raw), z: (batch, L, dim) float32 or bfloat16 on a GPU;
@@ -130,7 +133,8 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     (zeros; with h0 the call goes to mamba_scan_fwd_init). Returns
     (out, last_state) where out is (batch, L, dim) in x's dtype and last_state
     (batch, dim, N) float32 (None if not requested). ``segments`` > 0 forces
-    the number of time segments.
+    the number of time segments; ``zoh`` selects the exact zero-order-hold
+    input weight (MAMBA_SCAN_ZOH) instead of the first-order Delta B.
     """
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
@@ -158,7 +162,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    d = Desc(batch, L, dim, N, _IO[io], int(segments))
+    d = Desc(batch, L, dim, N, _IO[io], int(segments) | (ZOH_FLAG if zoh else 0))
     ws_bytes = int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     if h0 is None:
@@ -235,9 +239,11 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, *, h0=Non
     return g
 
 
-def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None):
+def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,
+                 zoh=False):
     """One decode token: advances ``state`` (batch, dim, N) float32 in place and
-    returns out (batch, dim). x, delta, z: (batch, dim); B, C: (batch, N)."""
+    returns out (batch, dim). x, delta, z: (batch, dim); B, C: (batch, N).
+    ``zoh`` selects the exact zero-order-hold input weight."""
     lib = load_library()
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, dim) and A (dim, N)")
@@ -260,7 +266,7 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _need(out, "out", (batch, dim), io, dev)
-    d = Desc(batch, 1, dim, N, _IO[io], 0)
+    d = Desc(batch, 1, dim, N, _IO[io], ZOH_FLAG if zoh else 0)
     st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(dev))

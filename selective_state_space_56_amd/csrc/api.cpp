@@ -95,7 +95,7 @@ const char* mamba_last_error(void) { return g_last_error.c_str(); }
 
 size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
   if (check_desc(d, "mamba_scan_workspace_size") != MAMBA_OK) return 0;
-  if (d->flags & ~0xffffu) return 0;
+  if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH)) return 0;
   return mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
                           forced_segments(d))
       .workspace_bytes;
@@ -112,8 +112,9 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
                            void* stream) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
-  if (d->flags & ~0xffffu)
-    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
+  if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH))
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who,
+                d->flags & ~(0xffffu | MAMBA_SCAN_ZOH));
   const int64_t rows = d->batch * d->dim;
   const int64_t tokens = d->batch * d->seqlen;
   const int64_t elems = tokens * d->dim;
@@ -198,6 +199,7 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   p.dim = d->dim;
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
+  p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
   const hipError_t e = mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -232,7 +234,8 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   const char* who = "mamba_state_update";
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
-  if (d->flags != 0) return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0", who);
+  if (d->flags & ~MAMBA_SCAN_ZOH)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0 or MAMBA_SCAN_ZOH", who);
   if (d->seqlen != 1)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
   if ((d->batch + 15) / 16 > 65535)
@@ -291,6 +294,7 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   p.dim = d->dim;
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
+  p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
   const hipError_t e = mscan::launch_state_update(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -442,6 +446,9 @@ namespace {
 mamba_status scan_bwd_check(const char* who, const mamba_scan_desc* d) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
+  if (d->flags & MAMBA_SCAN_ZOH)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: the backward of the MAMBA_SCAN_ZOH mode is not provided",
+                who);
   if (d->flags & ~0xffffu)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
   return MAMBA_OK;

@@ -119,4 +119,17 @@ __device__ __forceinline__ float silu_f(float v) {
   return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e));
 }
 
+// Exact zero-order-hold input weight ("Mamba and selective state spaces, from
+// first principles", section "Discretisation: zero-order hold"):
+// Bbar_n = (exp(Delta A_n) - 1) / A_n B_n = Delta zoh_gain(Delta A_n) B_n with
+// zoh_gain(v) = (e^v - 1) / v, given v2 = v log2(e) and e2 = 2^v2 = e^v. Near
+// v = 0 the quotient is formed as (e - 1) / ln(e) from the rounded e (Kahan's
+// form for expm1: the rounding of e cancels between numerator and
+// denominator); for e < 1/2 the direct quotient has no cancellation (and stays
+// right when e underflows); at e = 1 the gain is 1.
+__device__ __forceinline__ float zoh_gain(float v2, float e2) {
+  const float den = (e2 < 0.5f ? v2 : hw_log2(e2)) * kLn2;
+  return e2 == 1.0f ? 1.0f : (e2 - 1.0f) * hw_rcp(den);
+}
+
 }  // namespace mscan

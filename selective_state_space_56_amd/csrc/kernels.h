@@ -24,6 +24,7 @@ struct ScanProblem {
   int64_t batch, seqlen, dim;
   int dstate;
   int io;
+  bool zoh;            // exact zero-order-hold input weight instead of Delta
 };
 
 // Time segmentation of a full-sequence scan: the sequence is cut into
@@ -110,6 +111,7 @@ struct DecodeProblem {
   int64_t batch, dim;
   int dstate;
   int io;
+  bool zoh;            // exact zero-order-hold input weight instead of Delta
 };
 
 hipError_t launch_state_update(const DecodeProblem& p, hipStream_t stream);

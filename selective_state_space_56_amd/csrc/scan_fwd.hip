@@ -90,8 +90,9 @@ __device__ __forceinline__ FrontEnd front_end(typename IO::raw xr, typename IO::
 
 // State update, read-out and epilogue of one step. Returns y in the io type.
 // h holds g on structured rows; dx_prev is dx of the previous step there.
-// The read-out is one multiply-add per state.
-template <int N, class IO, int MODE, bool GATE, bool STRUCTURED>
+// The read-out is one multiply-add per state. ZOH (general rows only): the
+// input term takes the exact zero-order-hold weight instead of Delta.
+template <int N, class IO, int MODE, bool GATE, bool STRUCTURED, bool ZOH>
 __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const float (&bc)[2 * N],
                                                    const float (&A2)[N], float Dd, float (&h)[N],
                                                    float& dx_prev) {
@@ -111,7 +112,13 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
     y = Dd * f.xf;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      h[n] = fmaf(hw_exp2(f.Delta * A2[n]), h[n], f.dx * bc[n]);
+      if constexpr (ZOH) {
+        const float v2 = f.Delta * A2[n];
+        const float e2 = hw_exp2(v2);
+        h[n] = fmaf(e2, h[n], zoh_gain(v2, e2) * (f.dx * bc[n]));
+      } else {
+        h[n] = fmaf(hw_exp2(f.Delta * A2[n]), h[n], f.dx * bc[n]);
+      }
       if (MODE == kOutput) y = fmaf(bc[N + n], h[n], y);
     }
   }
@@ -153,8 +160,9 @@ struct __align__(16) Stage {
 // register-staged copy otherwise.
 // Decay paths compiled into one kernel: kPathGeneral (exp per state),
 // kPathStructured (powers of one exponential, for S4D-Real-shaped A), or both
-// behind a per-workgroup branch.
-enum PathSet { kPathGeneral = 0, kPathStructured = 1, kPathBoth = 2 };
+// behind a per-workgroup branch; kPathGeneralZoh: the general path with the
+// exact zero-order-hold input weight, for every tile.
+enum PathSet { kPathGeneral = 0, kPathStructured = 1, kPathBoth = 2, kPathGeneralZoh = 3 };
 
 #ifndef MSCAN_FUSED_PATHS
 #define MSCAN_FUSED_PATHS 0
@@ -219,7 +227,9 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   // group together): the launch for the other path writes its results.
   const unsigned tile = blockIdx.x % g.tiles;
   bool tile_structured;
-  if (g.tile_flags == nullptr || (MODE == kAggregate && PATHS != kPathGeneral)) {
+  if (PATHS == kPathGeneralZoh) {
+    tile_structured = false;
+  } else if (g.tile_flags == nullptr || (MODE == kAggregate && PATHS != kPathGeneral)) {
     bool structured = true;
     const float a0 = A[d * N];
 #pragma unroll
@@ -360,7 +370,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
                 kZ ? st.in[buf][kZi][js + 1][tid] : raw(0), A2[0], bias);
           float bc[2 * N];
           read_bc<N>(st.bc[buf][js], bc, kC);
-          const raw y = update<N, IO, MODE, GATE, KSTRUCT>(fe, bc, A2, Dd, h, dx_prev);
+          const raw y =
+              update<N, IO, MODE, GATE, KSTRUCT, PATHS == kPathGeneralZoh>(fe, bc, A2, Dd, h, dx_prev);
           if (MODE == kOutput) st.yo[buf][js][tid] = y;
           if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   };
   if (steps > 0) {
     if (tile_structured) {
-      if constexpr (PATHS != kPathGeneral) run(std::true_type{});
+      if constexpr (PATHS != kPathGeneral && PATHS != kPathGeneralZoh) run(std::true_type{});
     } else {
       if constexpr (PATHS != kPathStructured) run(std::false_type{});
     }
@@ -497,6 +508,29 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
 
   const dim3 block(kBlock);
   const unsigned blocks = g.tiles * static_cast<unsigned>(p.batch);
+  if (p.zoh) {
+    // exact zero-order hold: the general path, one launch per pass
+    if (plan.segments > 1) {
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, kPathGeneralZoh>),
+                         dim3(blocks, plan.segments - 1), block, 0, stream, x, dl, p.A, B, C, p.D,
+                         z, p.bias, out, p.last_state, ws_h, ws_s, g);
+      const int64_t work = g.rows * N;
+      hipLaunchKernelGGL((scan_combine_kernel<N>),
+                         dim3(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock)),
+                         dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s, p.h0, g.rows, p.dim,
+                         plan.segments);
+    }
+    const dim3 grid(blocks, plan.segments);
+    if (z)
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, true, CW, kPathGeneralZoh>), grid,
+                         block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state,
+                         ws_h, ws_s, g);
+    else
+      hipLaunchKernelGGL((scan_segment_kernel<N, IO, kOutput, false, CW, kPathGeneralZoh>), grid,
+                         block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out, p.last_state,
+                         ws_h, ws_s, g);
+    return hipGetLastError();
+  }
   // one launch per decay path, or one for both
   constexpr int kFirst = MSCAN_FUSED_PATHS ? kPathBoth : kPathStructured;
   constexpr bool kSecond = !MSCAN_FUSED_PATHS;

@@ -44,7 +44,8 @@ struct DecodeKernelArgs {
 
 // Grid: x = (channel, lane-of-row) pairs, kBlock per workgroup; y = runs of
 // kDecodeRows batch rows.
-template <int N, class IO>
+// ZOH: the input term takes the exact zero-order-hold weight instead of Delta.
+template <int N, class IO, bool ZOH>
 __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a) {
   using raw = typename IO::raw;
   constexpr int SPL = N >= 4 ? 4 : N;  // states per lane
@@ -106,8 +107,10 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a
       float y = 0.0f;
 #pragma unroll
       for (int k = 0; k < SPL; ++k) {
-        const float abar = hw_exp2(Delta * A2[k]);
-        h[r][k] = fmaf(abar, h[r][k], dx * Bv[r][k]);
+        const float v2 = Delta * A2[k];
+        const float abar = hw_exp2(v2);
+        const float bx = ZOH ? zoh_gain(v2, abar) * (dx * Bv[r][k]) : dx * Bv[r][k];
+        h[r][k] = fmaf(abar, h[r][k], bx);
         y = fmaf(Cv[r][k], h[r][k], y);
       }
 #pragma unroll
@@ -151,7 +154,10 @@ hipError_t launch_typed(const DecodeProblem& p, hipStream_t stream) {
   const int64_t threads = p.dim * LPR;
   const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock),
                   static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));
-  hipLaunchKernelGGL((state_update_kernel<N, IO>), grid, dim3(kBlock), 0, stream, a);
+  if (p.zoh)
+    hipLaunchKernelGGL((state_update_kernel<N, IO, true>), grid, dim3(kBlock), 0, stream, a);
+  else
+    hipLaunchKernelGGL((state_update_kernel<N, IO, false>), grid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 

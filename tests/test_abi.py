@@ -116,7 +116,7 @@ def test_scan_rejects_bad_descriptors(lib):
     for n in (3, 5, 32, 64):
         assert scan(lib, D_(dstate=n)) == UNSUPPORTED
         assert "dstate" in err(lib)
-    assert scan(lib, D_(flags=1 << 16)) == INVALID
+    assert scan(lib, D_(flags=1 << 17)) == INVALID
     assert scan(lib, D_(batch=1 << 20, dim=1 << 20)) == UNSUPPORTED
 
 
@@ -299,3 +299,24 @@ def test_scan_bwd_validation(lib):
     # nothing to do for dim == 0; dA is required otherwise, even with no steps
     assert bwd(lib, D_(dim=0), **{k: None for k in BWD_ARGS}) == 0
     assert bwd(lib, D_(seqlen=0), dA=None) == INVALID
+
+
+ZOH = 1 << 16
+
+
+def test_zoh_flag_validation(lib):
+    """MAMBA_SCAN_ZOH is accepted by the forward entry points, other high bits
+    are not; the decode call accepts ZOH but no segment bits; the backward of
+    the ZOH mode is reported unsupported."""
+    d = D_(batch=1, seqlen=64, dim=16)
+    dz_ = D_(batch=1, seqlen=64, dim=16, flags=ZOH)
+    assert lib.mamba_scan_workspace_size(ctypes.byref(dz_)) == lib.mamba_scan_workspace_size(ctypes.byref(d))
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(flags=1 << 17))) == 0
+    assert scan(lib, D_(flags=1 << 17)) == INVALID
+    assert "unknown flag bits" in err(lib)
+    assert upd(lib, D_(seqlen=1, flags=ZOH | 3)) == INVALID
+    assert "MAMBA_SCAN_ZOH" in err(lib)
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(dz_)) == 0
+    need = lib.mamba_scan_bwd_workspace_size(ctypes.byref(d))
+    assert bwd(lib, dz_, ws=40, ws_bytes=need) == UNSUPPORTED
+    assert "ZOH" in err(lib)
