@@ -45,6 +45,12 @@ def _f64(a, shape=None):
     return a
 
 
+def _groups(B):
+    """Number of channel groups of a (batch, L, N) or (batch, L, G, N) B."""
+    shp = np.asarray(B).shape
+    return shp[2] if len(shp) == 4 else 1
+
+
 class Oracle:
     """Thin handle on one compiled oracle library (the real one or a test
     mutant built from an edited copy of the source)."""
@@ -53,13 +59,11 @@ class Oracle:
         self.path = lib_path
         lib = ctypes.CDLL(lib_path)
         lib.oracle_scan_f64.restype = ctypes.c_int
-        lib.oracle_scan_f64.argtypes = [_i64, _i64, _i64, _i64] + [_dp] * 9 + \
-            [ctypes.c_int, _dp, _dp, ctypes.c_int]
+        lib.oracle_scan_f64.argtypes = [_i64] * 5 + [_dp] * 9 + [ctypes.c_int, _dp, _dp, ctypes.c_int]
         lib.oracle_state_update_f64.restype = ctypes.c_int
-        lib.oracle_state_update_f64.argtypes = [_i64, _i64, _i64] + [_dp] * 9 + \
-            [ctypes.c_int, _dp, ctypes.c_int]
+        lib.oracle_state_update_f64.argtypes = [_i64] * 4 + [_dp] * 9 + [ctypes.c_int, _dp, ctypes.c_int]
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
-        lib.oracle_scan_bwd_f64.argtypes = [_i64] * 4 + [_dp] * 20 + [ctypes.c_int]
+        lib.oracle_scan_bwd_f64.argtypes = [_i64] * 5 + [_dp] * 20 + [ctypes.c_int]
         lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         lib.oracle_conv1d_silu_f64.argtypes = [_i64] * 4 + [_dp] * 6 + [ctypes.c_int]
         lib.oracle_conv1d_update_f64.restype = ctypes.c_int
@@ -69,15 +73,17 @@ class Oracle:
     def scan(self, x, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
              zoh=False, nthreads=None):
         """Full-sequence scan. x, delta, z: (batch, L, dim); A: (dim, N);
-        B, C: (batch, L, N); D, delta_bias: (dim,); h0: (batch, dim, N).
-        Returns (out (batch, L, dim), last_state (batch, dim, N)) in fp64."""
+        B, C: (batch, L, N), or (batch, L, G, N) for G groups of channels;
+        D, delta_bias: (dim,); h0: (batch, dim, N). Returns (out (batch, L,
+        dim), last_state (batch, dim, N)) in fp64."""
         x = _f64(x)
         batch, L, dim = x.shape
         A = _f64(A)
         N = A.shape[1]
         delta = _f64(delta, x.shape)
-        B = _f64(B, (batch, L, N))
-        C = _f64(C, (batch, L, N))
+        G = _groups(B)
+        B = _f64(B, (batch, L, G, N))
+        C = _f64(C, (batch, L, G, N))
         D = _f64(D, (dim,))
         z = _f64(z, x.shape)
         delta_bias = _f64(delta_bias, (dim,))
@@ -85,7 +91,7 @@ class Oracle:
         out = np.empty((batch, L, dim), dtype=np.float64)
         last = np.empty((batch, dim, N), dtype=np.float64)
         nt = nthreads if nthreads else (os.cpu_count() or 1)
-        rc = self.lib.oracle_scan_f64(batch, L, dim, N, _ptr(x), _ptr(delta), _ptr(A),
+        rc = self.lib.oracle_scan_f64(batch, L, dim, N, G, _ptr(x), _ptr(delta), _ptr(A),
                                       _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                       _ptr(h0), int(bool(zoh)), _ptr(out), _ptr(last), nt)
         if rc != 0:
@@ -95,21 +101,23 @@ class Oracle:
     def state_update(self, state, x, delta, A, B, C, D=None, z=None, delta_bias=None,
                      zoh=False, nthreads=None):
         """One decode token. state: (batch, dim, N), updated copy returned;
-        x, delta, z: (batch, dim); B, C: (batch, N). Returns (out, new_state)."""
+        x, delta, z: (batch, dim); B, C: (batch, N), or (batch, G, N) for G
+        groups of channels. Returns (out, new_state)."""
         x = _f64(x)
         batch, dim = x.shape
         A = _f64(A)
         N = A.shape[1]
         st = np.array(_f64(state, (batch, dim, N)), dtype=np.float64, copy=True)
         delta = _f64(delta, x.shape)
-        B = _f64(B, (batch, N))
-        C = _f64(C, (batch, N))
+        G = np.asarray(B).shape[1] if np.asarray(B).ndim == 3 else 1
+        B = _f64(B, (batch, G, N))
+        C = _f64(C, (batch, G, N))
         D = _f64(D, (dim,))
         z = _f64(z, x.shape)
         delta_bias = _f64(delta_bias, (dim,))
         out = np.empty((batch, dim), dtype=np.float64)
         nt = nthreads if nthreads else (os.cpu_count() or 1)
-        rc = self.lib.oracle_state_update_f64(batch, dim, N, _ptr(st), _ptr(x), _ptr(delta),
+        rc = self.lib.oracle_state_update_f64(batch, dim, N, G, _ptr(st), _ptr(x), _ptr(delta),
                                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                               _ptr(delta_bias), int(bool(zoh)), _ptr(out), nt)
         if rc != 0:
@@ -121,15 +129,17 @@ class Oracle:
                  dlast=None, nthreads=None):
         """Gradients of the scan (first-order B-bar) for dLoss/dout and
         optionally dLoss/dlast_state. Returns a dict with dx, ddelta, dz
-        (batch, L, dim), dA (dim, N), dB, dC (batch, L, N), dD, dbias (dim,)
-        and dh0 (batch, dim, N), all fp64."""
+        (batch, L, dim), dA (dim, N), dB, dC (the shape of B: (batch, L, N) or
+        (batch, L, G, N)), dD, dbias (dim,) and dh0 (batch, dim, N), all fp64."""
         x = _f64(x)
         batch, L, dim = x.shape
         A = _f64(A)
         N = A.shape[1]
         delta = _f64(delta, x.shape)
-        B = _f64(B, (batch, L, N))
-        C = _f64(C, (batch, L, N))
+        bshape = np.asarray(B).shape
+        G = _groups(B)
+        B = _f64(B, (batch, L, G, N))
+        C = _f64(C, (batch, L, G, N))
         D = _f64(D, (dim,))
         z = _f64(z, x.shape)
         delta_bias = _f64(delta_bias, (dim,))
@@ -137,11 +147,11 @@ class Oracle:
         dout = _f64(dout, x.shape)
         dlast = _f64(dlast, (batch, dim, N))
         g = {"dx": np.empty(x.shape), "ddelta": np.empty(x.shape), "dA": np.empty((dim, N)),
-             "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N)), "dD": np.empty(dim),
+             "dB": np.empty(bshape), "dC": np.empty(bshape), "dD": np.empty(dim),
              "dz": np.empty(x.shape), "dbias": np.empty(dim), "dh0": np.empty((batch, dim, N))}
         nt = nthreads if nthreads else (os.cpu_count() or 1)
         rc = self.lib.oracle_scan_bwd_f64(
-            batch, L, dim, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            batch, L, dim, N, G, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
             _ptr(delta_bias), _ptr(h0), _ptr(dout), _ptr(dlast), _ptr(g["dx"]), _ptr(g["ddelta"]),
             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
             _ptr(g["dbias"]), _ptr(g["dh0"]), nt)

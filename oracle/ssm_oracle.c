@@ -41,8 +41,12 @@
  *   last_state[b,d,:] = h
  *
  * Layouts (row-major, contiguous): x, delta, z, out: (batch, seqlen, dim);
- * B, C: (batch, seqlen, dstate), one group shared by every channel; A:
- * (dim, dstate); D, bias: (dim); h0, last_state, state: (batch, dim, dstate).
+ * B, C: (batch, seqlen, ngroups, dstate): the channels form ngroups equal
+ * consecutive groups, channel d reading group d / (dim / ngroups) (one group
+ * shared by every channel is the S6 layer of ai.thesatyajit.com, "Selection";
+ * groups of channels sharing B and C are the grouping of the same page's
+ * "Mamba-2" section); A: (dim, dstate); D, bias: (dim); h0, last_state,
+ * state: (batch, dim, dstate).
  * Optional arguments are NULL when absent (no D skip, no gate, zero bias, zero
  * initial state, no final state).
  *
@@ -92,28 +96,31 @@ static double row_step(int64_t N, double *h, double x, double delta_raw,
  * required pointer, -2 when zoh is requested with a zero entry of A.
  */
 int oracle_scan_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                    const double *x, const double *delta, const double *A,
+                    int64_t ngroups, const double *x, const double *delta, const double *A,
                     const double *B, const double *C, const double *D,
                     const double *z, const double *delta_bias,
                     const double *h0, int zoh, double *out, double *last_state,
                     int nthreads) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1) return -1;
+  if (ngroups < 1 || dim % ngroups != 0) return -1;
   if (!x || !delta || !A || !B || !C || !out) return -1;
   if (zoh)
     for (int64_t i = 0; i < dim * dstate; ++i)
       if (A[i] == 0.0) return -2;
   if (nthreads < 1) nthreads = 1;
+  const int64_t per_group = dim / ngroups;
 
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
   for (int64_t b = 0; b < batch; ++b) {
     for (int64_t d = 0; d < dim; ++d) {
+      const int64_t g = d / per_group;
       double *h = (double *)malloc(sizeof(double) * (size_t)dstate);
       for (int64_t n = 0; n < dstate; ++n)
         h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
       double bias = delta_bias ? delta_bias[d] : 0.0;
       for (int64_t t = 0; t < seqlen; ++t) {
         int64_t i = (b * seqlen + t) * dim + d;   /* (b, t, d) */
-        int64_t j = (b * seqlen + t) * dstate;    /* (b, t, 0) */
+        int64_t j = ((b * seqlen + t) * ngroups + g) * dstate; /* (b, t, g, 0) */
         out[i] = row_step(dstate, h, x[i], delta[i], bias, A + d * dstate,
                           B + j, C + j, D ? D + d : NULL, z ? z + i : NULL, zoh);
       }
@@ -129,28 +136,31 @@ int oracle_scan_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 /*
  * One decode token for every (b, d) row: the same step as one iteration of
  * the scan, against a resident state that is read and written in place.
- * x, delta, z, out: (batch, dim); B, C: (batch, dstate).
+ * x, delta, z, out: (batch, dim); B, C: (batch, ngroups, dstate).
  */
-int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate,
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t ngroups,
                             double *state, const double *x,
                             const double *delta, const double *A,
                             const double *B, const double *C, const double *D,
                             const double *z, const double *delta_bias, int zoh,
                             double *out, int nthreads) {
   if (batch < 0 || dim < 0 || dstate < 1) return -1;
+  if (ngroups < 1 || dim % ngroups != 0) return -1;
   if (!state || !x || !delta || !A || !B || !C || !out) return -1;
   if (zoh)
     for (int64_t i = 0; i < dim * dstate; ++i)
       if (A[i] == 0.0) return -2;
   if (nthreads < 1) nthreads = 1;
+  const int64_t per_group = dim / ngroups;
 
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
   for (int64_t b = 0; b < batch; ++b) {
     for (int64_t d = 0; d < dim; ++d) {
       int64_t i = b * dim + d;
+      int64_t j = (b * ngroups + d / per_group) * dstate; /* (b, g, 0) */
       out[i] = row_step(dstate, state + i * dstate, x[i], delta[i],
                         delta_bias ? delta_bias[d] : 0.0, A + d * dstate,
-                        B + b * dstate, C + b * dstate, D ? D + d : NULL,
+                        B + j, C + j, D ? D + d : NULL,
                         z ? z + i : NULL, zoh);
     }
   }
@@ -257,32 +267,33 @@ int oracle_conv1d_update_f64(int64_t batch, int64_t dim, int64_t width, double *
  * and, from h_t = abar_t h_{t-1} + Delta_t x_t B_t with abar_t = exp(Delta_t A):
  *   dDelta_t = sum_n lambda_t,n (A_n abar_t,n h_{t-1,n} + x_t B_t,n)
  *   dx_t     = D ds_t + sum_n lambda_t,n Delta_t B_t,n
- *   dB_t,n  += lambda_t,n Delta_t x_t          (summed over channels)
- *   dC_t,n  += ds_t h_t,n                       (summed over channels)
+ *   dB_t,n  += lambda_t,n Delta_t x_t          (summed over the group's channels)
+ *   dC_t,n  += ds_t h_t,n                       (summed over the group's channels)
  *   dA_n    += lambda_t,n Delta_t abar_t,n h_{t-1,n}  (summed over batch, time)
  *   dz_t     = dout_t s_t silu'(z_t)
  *   ddelta_t = dDelta_t sigmoid(delta_t + bias)  (softplus' = sigmoid)
  *   dbias   += ddelta_t; dD += ds_t x_t;  dh0 = abar_0 lambda_0.
  * Outputs: dx, ddelta, dz (batch, seqlen, dim); dA (dim, dstate); dB, dC
- * (batch, seqlen, dstate); dD, dbias (dim); dh0 (batch, dim, dstate). dz, dD,
+ * (batch, seqlen, ngroups, dstate); dD, dbias (dim); dh0 (batch, dim, dstate). dz, dD,
  * dbias, dh0 may be NULL (not wanted); all outputs are overwritten.
  * Parallel over channels; dB and dC are accumulated per thread, then summed.
  */
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-                        const double *x, const double *delta, const double *A,
+                        int64_t ngroups, const double *x, const double *delta, const double *A,
                         const double *B, const double *C, const double *D,
                         const double *z, const double *delta_bias, const double *h0,
                         const double *dout, const double *dlast, double *dx,
                         double *ddelta, double *dA, double *dB, double *dC, double *dD,
                         double *dz, double *dbias, double *dh0, int nthreads) {
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > 64) return -1;
+  if (ngroups < 1 || dim % ngroups != 0) return -1;
   if (!x || !delta || !A || !B || !C || !dout || !dx || !ddelta || !dA || !dB || !dC)
     return -1;
   if (nthreads < 1) nthreads = 1;
-  const int64_t N = dstate, L = seqlen;
-  const int64_t bcn = batch * L * N;
+  const int64_t N = dstate, L = seqlen, G = ngroups, per_group = dim / ngroups;
+  const int64_t bcn = batch * L * G * N;
   double *part = (double *)calloc((size_t)(nthreads * 2 * bcn + 1), sizeof(double));
   double *hist = (double *)malloc((size_t)(nthreads * (L + 1) * N + 1) * sizeof(double));
   if (!part || !hist) {
@@ -305,7 +316,7 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
     for (int64_t b = 0; b < batch; ++b) {
       for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
       for (int64_t t = 0; t < L; ++t) {
-        const int64_t i = (b * L + t) * dim + d, j = (b * L + t) * N;
+        const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d / per_group) * N;
         const double Dl = softplus(delta[i] + bias);
         for (int64_t n = 0; n < N; ++n)
           hs[(t + 1) * N + n] = exp(Dl * A_d[n]) * hs[t * N + n] + Dl * B[j + n] * x[i];
@@ -313,7 +324,7 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
       double lam[64];
       for (int64_t n = 0; n < N; ++n) lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;
       for (int64_t t = L - 1; t >= 0; --t) {
-        const int64_t i = (b * L + t) * dim + d, j = (b * L + t) * N;
+        const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d / per_group) * N;
         const double u = delta[i] + bias, Dl = softplus(u), xt = x[i];
         double s = D ? D[d] * xt : 0.0;
         for (int64_t n = 0; n < N; ++n) s += C[j + n] * hs[(t + 1) * N + n];

@@ -547,7 +547,57 @@ def pin_bwd_readout_only(orc):
     _close(g["dC"], want, 1e-12, 1e-13, "dC")
 
 
-BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_bare, pin_bwd_readout_only]
+def pin_groups_decompose(orc):
+    """Channels in G groups, each group with its own B_t, C_t: the scan, the
+    one-token update and every gradient equal G single-group problems on the
+    channel slices (rows never mix; a group's B and C reach only its
+    channels)."""
+    rng = np.random.default_rng(51)
+    batch, L, dim, N, G = 2, 9, 6, 4, 3
+    per = dim // G
+    x, delta, z = rng.normal(size=(3, batch, L, dim))
+    A = -rng.uniform(0.2, 2, (dim, N))
+    B = rng.normal(size=(batch, L, G, N))
+    C = rng.normal(size=(batch, L, G, N))
+    D = rng.normal(size=dim)
+    bias = rng.normal(0, .5, dim)
+    h0 = rng.normal(size=(batch, dim, N))
+    dout = rng.normal(size=(batch, L, dim))
+    dlast = rng.normal(size=(batch, dim, N))
+    y, last = orc.scan(x, delta, A, B, C, D=D, z=z, delta_bias=bias, h0=h0)
+    g = orc.scan_bwd(x, delta, A, B, C, dout, D=D, z=z, delta_bias=bias, h0=h0, dlast=dlast)
+    st = h0.copy()
+    ys_dec = []
+    for t in range(3):
+        o, st = orc.state_update(st, x[:, t], delta[:, t], A, B[:, t], C[:, t], D=D, z=z[:, t],
+                                 delta_bias=bias)
+        ys_dec.append(o)
+    for k in range(G):
+        sl = slice(k * per, (k + 1) * per)
+        ys, ls = orc.scan(x[:, :, sl], delta[:, :, sl], A[sl], B[:, :, k], C[:, :, k], D=D[sl],
+                          z=z[:, :, sl], delta_bias=bias[sl], h0=h0[:, sl])
+        _close(y[:, :, sl], ys, 1e-15, 1e-15, f"group {k} y")
+        _close(last[:, sl], ls, 1e-15, 1e-15, f"group {k} last state")
+        gs = orc.scan_bwd(x[:, :, sl], delta[:, :, sl], A[sl], B[:, :, k], C[:, :, k], dout[:, :, sl],
+                          D=D[sl], z=z[:, :, sl], delta_bias=bias[sl], h0=h0[:, sl],
+                          dlast=dlast[:, sl])
+        for key in ("dx", "ddelta", "dz"):
+            _close(g[key][:, :, sl], gs[key], 1e-13, 1e-15, f"group {k} {key}")
+        for key in ("dA", "dD", "dbias"):
+            _close(g[key][sl], gs[key], 1e-13, 1e-15, f"group {k} {key}")
+        _close(g["dh0"][:, sl], gs["dh0"], 1e-13, 1e-15, f"group {k} dh0")
+        _close(g["dB"][:, :, k], gs["dB"], 1e-13, 1e-15, f"group {k} dB")
+        _close(g["dC"][:, :, k], gs["dC"], 1e-13, 1e-15, f"group {k} dC")
+        sts = h0[:, sl].copy()
+        for t in range(3):
+            o, sts = orc.state_update(sts, x[:, t, sl], delta[:, t, sl], A[sl], B[:, t, k],
+                                      C[:, t, k], D=D[sl], z=z[:, t, sl], delta_bias=bias[sl])
+            _close(ys_dec[t][:, sl], o, 1e-15, 1e-15, f"group {k} decode step {t}")
+        _close(st[:, sl], sts, 1e-15, 1e-15, f"group {k} decode state")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_bare, pin_bwd_readout_only,
+            pin_groups_decompose]
 
 
 # ---------------------------------------------------------------------------

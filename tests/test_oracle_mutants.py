@@ -33,8 +33,8 @@ MUTATIONS = [
     ("drop_bias", "double Delta = softplus(delta_raw + bias);", "double Delta = softplus(delta_raw);"),
     ("A_row_index", "A + d * dstate,\n                          B + j", "A + d,\n                          B + j"),
     ("nonzero_init", "h0[(b * dim + d) * dstate + n] : 0.0;", "h0[(b * dim + d) * dstate + n] : 1.0;"),
-    ("BC_time_off_by_one", "int64_t j = (b * seqlen + t) * dstate;",
-     "int64_t j = (b * seqlen + (t > 0 ? t - 1 : t)) * dstate;"),
+    ("BC_time_off_by_one", "int64_t j = ((b * seqlen + t) * ngroups + g) * dstate;",
+     "int64_t j = ((b * seqlen + (t > 0 ? t - 1 : t)) * ngroups + g) * dstate;"),
     ("sigmoid_sign", "return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
     ("readout_before_update", "h[n] = abar * h[n] + bbar * x;\n    y += C_t[n] * h[n];",
      "y += C_t[n] * h[n];\n    h[n] = abar * h[n] + bbar * x;"),
@@ -43,7 +43,7 @@ MUTATIONS = [
     ("zoh_sign", "bbar = (abar - 1.0) / A_d[n] * B_t[n];", "bbar = (1.0 - abar) / A_d[n] * B_t[n];"),
     ("decode_state_row", "out[i] = row_step(dstate, state + i * dstate",
      "out[i] = row_step(dstate, state + d * dstate"),
-    ("decode_BC_swap", "B + b * dstate, C + b * dstate", "C + b * dstate, B + b * dstate"),
+    ("decode_BC_swap", "B + j, C + j, D ? D + d : NULL,\n", "C + j, B + j, D ? D + d : NULL,\n"),
     ("last_state_layout", "last_state[(b * dim + d) * dstate + n] = h[n];",
      "last_state[(d * batch + b) * dstate + n] = h[n];"),
     ("x_layout", "int64_t i = (b * seqlen + t) * dim + d;   /* (b, t, d) */",
@@ -57,6 +57,13 @@ MUTATIONS = [
     ("bwd_dA_without_abar", "dA_acc[n] += lam[n] * Dl * abar * hprev;", "dA_acc[n] += lam[n] * Dl * hprev;"),
     ("bwd_dx_without_D", "double dDl = 0.0, dxt = D ? D[d] * ds : 0.0;", "double dDl = 0.0, dxt = 0.0;"),
     ("bwd_softplus_grad_sign", "ddelta[i] = dDl * sigmoid(u);", "ddelta[i] = dDl * sigmoid(-u);"),
+    ("scan_group_index", "int64_t j = ((b * seqlen + t) * ngroups + g) * dstate;",
+     "int64_t j = ((b * seqlen + t) * ngroups + d % ngroups) * dstate;"),
+    ("decode_group_index", "int64_t j = (b * ngroups + d / per_group) * dstate;",
+     "int64_t j = (b * ngroups + d % ngroups) * dstate;"),
+    ("bwd_group_index",
+     "const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d / per_group) * N;\n        const double u",
+     "const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d % G) * N;\n        const double u"),
     ("bwd_dz_silu_grad", "dz[i] = dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg));",
      "dz[i] = dout[i] * s * sg;"),
     ("bwd_dlast_dropped", "lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
