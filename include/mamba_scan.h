@@ -93,7 +93,21 @@ typedef struct mamba_scan_desc {
   int64_t dstate;  /* N                                            */
   int32_t io_dtype;/* mamba_dtype of x, delta, z, B, C and out     */
   uint32_t flags;  /* see above                                    */
+  int64_t ngroups; /* G: groups of channels with their own B and C
+                      (0 or 1: one group shared by every channel)  */
 } mamba_scan_desc;
+
+/*
+ * Groups. With G = ngroups > 1 the channels form G equal consecutive groups
+ * and channel d reads the B and C of group d / (dim / G): B and C have the
+ * shape (batch, seqlen, G, dstate) (decode: (batch, G, dstate)). One group is
+ * the S6 layer ("Mamba and selective state spaces, from first principles",
+ * section "Selection": N numbers of B and C per token, shared by every
+ * channel); channels grouped to share B and C are the grouping the same page
+ * describes in its section "Mamba-2". dim must be a multiple of G; for the
+ * full-sequence entry points each group must also be a whole number of
+ * 256-channel tiles (dim / G a multiple of 256), else MAMBA_ERR_UNSUPPORTED.
+ */
 
 /*
  * Bytes of device workspace mamba_scan_fwd needs for this problem (0 when
@@ -110,7 +124,8 @@ size_t mamba_scan_workspace_size(const mamba_scan_desc *desc);
  *   x, delta, z : (batch, seqlen, dim) io dtype. delta is Delta_raw, before the
  *                 bias and the softplus. z may be NULL (no gate).
  *   A           : (dim, dstate) float32.
- *   B, C        : (batch, seqlen, dstate) io dtype, shared by all channels.
+ *   B, C        : (batch, seqlen, G, dstate) io dtype (G = max(1, ngroups)):
+ *                 group g is shared by channels g * dim / G .. (g + 1) * dim / G - 1.
  *   D           : (dim) float32 or NULL (no direct term).
  *   delta_bias  : (dim) float32 or NULL (zero bias).
  *   out         : (batch, seqlen, dim) io dtype, written.
@@ -157,7 +172,7 @@ mamba_status mamba_scan_fwd_init(const mamba_scan_desc *desc, const void *x,
  *   state       : (batch, dim, dstate) float32, read and overwritten in place
  *                 with the state after this token.
  *   x, delta, z : (batch, dim) io dtype (z may be NULL).
- *   B, C        : (batch, dstate) io dtype.
+ *   B, C        : (batch, G, dstate) io dtype.
  *   A, D, delta_bias : as in mamba_scan_fwd.
  *   out         : (batch, dim) io dtype, written; must not overlap any input.
  */

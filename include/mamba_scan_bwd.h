@@ -20,8 +20,8 @@
  *   ddelta_t   = sigmoid(delta_t + delta_bias) sum_n lam_t,n (A_n abar_t,n h_{t-1},n + B_t,n x_t)
  *   dz_t       = dout_t (C_t . h_t + D x_t) silu'(z_t)
  *   dA[d,n]    = sum_{b,t} Delta_t lam_t,n abar_t,n h_{t-1},n
- *   dB[b,t,n]  = sum_d lam_t,n Delta_t x_t
- *   dC[b,t,n]  = sum_d ds_t h_t,n
+ *   dB[b,t,g,n] = sum_{d in group g} lam_t,n Delta_t x_t
+ *   dC[b,t,g,n] = sum_{d in group g} ds_t h_t,n
  *   dD[d]      = sum_{b,t} ds_t x_t
  *   ddelta_bias[d] = sum_{b,t} ddelta_t
  *   dh0        = abar_0 lam_0       (the gradient of the initial state)
@@ -69,7 +69,8 @@ size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc *desc);
  *   dz          : (batch, seqlen, dim) io dtype, written, or NULL to skip;
  *                 not touched when z is NULL.
  *   dA          : (dim, dstate) float32, written.
- *   dB, dC      : (batch, seqlen, dstate) float32, written.
+ *   dB, dC      : (batch, seqlen, G, dstate) float32 (the shape of B),
+ *                 written; each is summed over its group's channels.
  *   dD, ddelta_bias : (dim) float32 or NULL (skip), written.
  *   dh0         : (batch, dim, dstate) float32 or NULL (skip), written.
  *   workspace   : at least mamba_scan_bwd_workspace_size(desc) bytes, 256-byte

@@ -30,7 +30,14 @@ class MambaScanError(RuntimeError):
 
 class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
-                ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("ngroups", ctypes.c_int64)]
+
+
+def _groups(B, time_axis=True):
+    """G of a B/C tensor: (batch, L, G, N) / (batch, G, N) give G, the
+    ungrouped (batch, L, N) / (batch, N) give 1."""
+    return B.shape[-2] if B.dim() == (4 if time_axis else 3) else 1
 
 
 class ConvDesc(ctypes.Structure):
@@ -128,7 +135,8 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     """Selective scan over full sequences.
 
     x, delta (Delta_raw), z: (batch, L, dim) float32 or bfloat16 on a GPU;
-    A: (dim, N) float32; B, C: (batch, L, N) in x's dtype; D, delta_bias:
+    A: (dim, N) float32; B, C: (batch, L, N), or (batch, L, G, N) for G
+    groups of channels, in x's dtype; D, delta_bias:
     (dim,) float32 or None; h0: (batch, dim, N) float32 initial state or None
     (zeros; with h0 the call goes to mamba_scan_fwd_init). Returns
     (out, last_state) where out is (batch, L, dim) in x's dtype and last_state
@@ -149,8 +157,10 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
         raise TypeError(f"unsupported io dtype {io}")
     _need(delta, "delta", (batch, L, dim), io, dev)
     _need(z, "z", (batch, L, dim), io, dev)
-    _need(B, "B", (batch, L, N), io, dev)
-    _need(C, "C", (batch, L, N), io, dev)
+    G = _groups(B)
+    bshape = (batch, L, G, N) if B.dim() == 4 else (batch, L, N)
+    _need(B, "B", bshape, io, dev)
+    _need(C, "C", bshape, io, dev)
     _need(A, "A", (dim, N), torch.float32, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
@@ -162,7 +172,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    d = Desc(batch, L, dim, N, _IO[io], int(segments) | (ZOH_FLAG if zoh else 0))
+    d = Desc(batch, L, dim, N, _IO[io], int(segments) | (ZOH_FLAG if zoh else 0), G)
     ws_bytes = int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     if h0 is None:
@@ -208,8 +218,10 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, *, h0=Non
     _need(delta, "delta", (batch, L, dim), io, dev)
     _need(z, "z", (batch, L, dim), io, dev)
     _need(dout, "dout", (batch, L, dim), io, dev)
-    _need(B, "B", (batch, L, N), io, dev)
-    _need(C, "C", (batch, L, N), io, dev)
+    G = _groups(B)
+    bshape = (batch, L, G, N) if B.dim() == 4 else (batch, L, N)
+    _need(B, "B", bshape, io, dev)
+    _need(C, "C", bshape, io, dev)
     _need(A, "A", (dim, N), torch.float32, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
@@ -221,13 +233,13 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, *, h0=Non
         "ddelta": torch.empty((batch, L, dim), dtype=io, device=dev),
         "dz": torch.empty((batch, L, dim), dtype=io, device=dev) if (z is not None and want_dz) else None,
         "dA": torch.empty((dim, N), **f32),
-        "dB": torch.empty((batch, L, N), **f32),
-        "dC": torch.empty((batch, L, N), **f32),
+        "dB": torch.empty(bshape, **f32),
+        "dC": torch.empty(bshape, **f32),
         "dD": torch.empty((dim,), **f32),
         "ddelta_bias": torch.empty((dim,), **f32),
         "dh0": torch.empty((batch, dim, N), **f32) if want_dh0 else None,
     }
-    d = Desc(batch, L, dim, N, _IO[io], int(segments))
+    d = Desc(batch, L, dim, N, _IO[io], int(segments), G)
     ws_bytes = int(lib.mamba_scan_bwd_workspace_size(ctypes.byref(d)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     st = lib.mamba_scan_bwd(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
@@ -258,15 +270,17 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     _need(state, "state", (batch, dim, N), torch.float32, dev)
     _need(delta, "delta", (batch, dim), io, dev)
     _need(z, "z", (batch, dim), io, dev)
-    _need(B, "B", (batch, N), io, dev)
-    _need(C, "C", (batch, N), io, dev)
+    G = _groups(B, time_axis=False)
+    bshape = (batch, G, N) if B.dim() == 3 else (batch, N)
+    _need(B, "B", bshape, io, dev)
+    _need(C, "C", bshape, io, dev)
     _need(A, "A", (dim, N), torch.float32, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
     _need(out, "out", (batch, dim), io, dev)
-    d = Desc(batch, 1, dim, N, _IO[io], ZOH_FLAG if zoh else 0)
+    d = Desc(batch, 1, dim, N, _IO[io], ZOH_FLAG if zoh else 0, G)
     st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                                 _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
                                 _stream(dev))

@@ -77,6 +77,25 @@ mamba_status check_desc(const mamba_scan_desc* d, const char* who) {
 
 int forced_segments(const mamba_scan_desc* d) { return static_cast<int>(d->flags & 0xffffu); }
 
+int64_t groups_of(const mamba_scan_desc* d) { return d->ngroups > 1 ? d->ngroups : 1; }
+
+// Channel groups: G must divide dim; the full-sequence kernels stage one
+// group's B and C per 256-channel tile, so there each group must be a whole
+// number of tiles.
+mamba_status check_groups(const mamba_scan_desc* d, const char* who, bool tiles) {
+  if (d->ngroups < 0)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: ngroups %lld < 0", who, (long long)d->ngroups);
+  const int64_t G = groups_of(d);
+  if (G > 1 && (d->dim % G) != 0)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: dim %lld is not a multiple of ngroups %lld", who,
+                (long long)d->dim, (long long)G);
+  if (G > 1 && tiles && (d->dim / G) % 256 != 0)
+    return fail(MAMBA_ERR_UNSUPPORTED,
+                "%s: with %lld groups each group must be a multiple of 256 channels", who,
+                (long long)G);
+  return MAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,6 +115,7 @@ const char* mamba_last_error(void) { return g_last_error.c_str(); }
 size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
   if (check_desc(d, "mamba_scan_workspace_size") != MAMBA_OK) return 0;
   if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH)) return 0;
+  if (check_groups(d, "mamba_scan_workspace_size", true) != MAMBA_OK) return 0;
   return mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
                           forced_segments(d))
       .workspace_bytes;
@@ -115,6 +135,8 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH))
     return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who,
                 d->flags & ~(0xffffu | MAMBA_SCAN_ZOH));
+  if ((st = check_groups(d, who, true)) != MAMBA_OK) return st;
+  const int64_t G = groups_of(d);
   const int64_t rows = d->batch * d->dim;
   const int64_t tokens = d->batch * d->seqlen;
   const int64_t elems = tokens * d->dim;
@@ -144,8 +166,8 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
       {"x", x, static_cast<size_t>(elems) * eb},
       {"delta", delta, static_cast<size_t>(elems) * eb},
       {"z", z, static_cast<size_t>(elems) * eb},
-      {"B", B, static_cast<size_t>(tokens) * N * eb},
-      {"C", C, static_cast<size_t>(tokens) * N * eb},
+      {"B", B, static_cast<size_t>(tokens * G) * N * eb},
+      {"C", C, static_cast<size_t>(tokens * G) * N * eb},
       {"A", A, static_cast<size_t>(d->dim) * N * 4},
       {"D", D, static_cast<size_t>(d->dim) * 4},
       {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
@@ -200,6 +222,7 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
   p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
+  p.ngroups = G;
   const hipError_t e = mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -236,6 +259,8 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   if (st != MAMBA_OK) return st;
   if (d->flags & ~MAMBA_SCAN_ZOH)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0 or MAMBA_SCAN_ZOH", who);
+  if ((st = check_groups(d, who, false)) != MAMBA_OK) return st;
+  const int64_t G = groups_of(d);
   if (d->seqlen != 1)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
   if ((d->batch + 15) / 16 > 65535)
@@ -255,8 +280,8 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
       {"x", x, static_cast<size_t>(rows) * eb},
       {"delta", delta, static_cast<size_t>(rows) * eb},
       {"z", z, static_cast<size_t>(rows) * eb},
-      {"B", B, static_cast<size_t>(d->batch) * N * eb},
-      {"C", C, static_cast<size_t>(d->batch) * N * eb},
+      {"B", B, static_cast<size_t>(d->batch * G) * N * eb},
+      {"C", C, static_cast<size_t>(d->batch * G) * N * eb},
       {"A", A, static_cast<size_t>(d->dim) * N * 4},
       {"D", D, static_cast<size_t>(d->dim) * 4},
       {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
@@ -295,6 +320,7 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
   p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
+  p.ngroups = G;
   const hipError_t e = mscan::launch_state_update(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -451,7 +477,7 @@ mamba_status scan_bwd_check(const char* who, const mamba_scan_desc* d) {
                 who);
   if (d->flags & ~0xffffu)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
-  return MAMBA_OK;
+  return check_groups(d, who, true);
 }
 
 mscan::ScanBwdPlan bwd_plan(const mamba_scan_desc* d) {
@@ -464,7 +490,8 @@ mscan::ScanBwdPlan bwd_plan(const mamba_scan_desc* d) {
 extern "C" {
 
 size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc* d) {
-  if (!d || check_desc(d, "mamba_scan_bwd_workspace_size") != MAMBA_OK || (d->flags & ~0xffffu))
+  if (!d || check_desc(d, "mamba_scan_bwd_workspace_size") != MAMBA_OK || (d->flags & ~0xffffu) ||
+      check_groups(d, "mamba_scan_bwd_workspace_size", true) != MAMBA_OK)
     return 0;
   return bwd_plan(d).workspace_bytes;
 }
@@ -482,6 +509,7 @@ mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void*
   const int64_t rows = d->batch * d->dim;
   const int64_t tokens = d->batch * d->seqlen;
   const int64_t elems = tokens * d->dim;
+  const int64_t G = groups_of(d);
   if (d->dim == 0) return ok();
   if (!dA) return fail(MAMBA_ERR_INVALID_ARG, "%s: dA is NULL", who);
   if (elems > 0) {
@@ -513,8 +541,8 @@ mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void*
       {"delta", delta, E},
       {"z", z, E},
       {"dout", dout, E},
-      {"B", B, static_cast<size_t>(tokens) * N * eb},
-      {"C", C, static_cast<size_t>(tokens) * N * eb},
+      {"B", B, static_cast<size_t>(tokens * G) * N * eb},
+      {"C", C, static_cast<size_t>(tokens * G) * N * eb},
       {"A", A, static_cast<size_t>(d->dim) * N * 4},
       {"D", D, static_cast<size_t>(d->dim) * 4},
       {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
@@ -526,8 +554,8 @@ mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void*
       {"ddelta", ddelta, E},
       {"dz", z ? dz : nullptr, E},
       {"dA", dA, static_cast<size_t>(d->dim) * N * 4},
-      {"dB", dB, static_cast<size_t>(tokens) * N * 4},
-      {"dC", dC, static_cast<size_t>(tokens) * N * 4},
+      {"dB", dB, static_cast<size_t>(tokens * G) * N * 4},
+      {"dC", dC, static_cast<size_t>(tokens * G) * N * 4},
       {"dD", dD, static_cast<size_t>(d->dim) * 4},
       {"ddelta_bias", ddelta_bias, static_cast<size_t>(d->dim) * 4},
       {"dh0", dh0, static_cast<size_t>(rows) * N * 4},
@@ -577,6 +605,7 @@ mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void*
   p.dim = d->dim;
   p.dstate = static_cast<int>(d->dstate);
   p.io = d->io_dtype;
+  p.ngroups = G;
   const hipError_t e = mscan::launch_scan_bwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));

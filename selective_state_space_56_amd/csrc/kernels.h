@@ -25,6 +25,7 @@ struct ScanProblem {
   int dstate;
   int io;
   bool zoh;            // exact zero-order-hold input weight instead of Delta
+  int64_t ngroups;     // G >= 1: B, C are (batch, seqlen, G, dstate); dim / G a multiple of 256
 };
 
 // Time segmentation of a full-sequence scan: the sequence is cut into
@@ -81,6 +82,7 @@ struct ScanBwdProblem {
   int64_t batch, seqlen, dim;
   int dstate;
   int io;
+  int64_t ngroups;     // G >= 1: B, C, dB, dC are (batch, seqlen, G, dstate)
 };
 
 // Time segmentation and byte offsets of the backward's workspace regions
@@ -112,6 +114,7 @@ struct DecodeProblem {
   int dstate;
   int io;
   bool zoh;            // exact zero-order-hold input weight instead of Delta
+  int64_t ngroups;     // G >= 1 dividing dim: B, C are (batch, G, dstate)
 };
 
 hipError_t launch_state_update(const DecodeProblem& p, hipStream_t stream);

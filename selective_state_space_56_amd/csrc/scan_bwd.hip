@@ -54,6 +54,7 @@ struct BwdDims {
   int64_t batch, seqlen, dim, rows, seg_len;
   int segments;
   unsigned tiles;
+  int64_t ngroups, group_dim;  // B/C groups and channels per group
 };
 
 // Pointers of one backward call. carry_h / carry_hs: the end state from zero
@@ -211,7 +212,7 @@ struct TileCtx {
   static constexpr int kTileElems = kChunk * 2 * N;
   static constexpr int kBcPer = (kTileElems + kBlock - 1) / kBlock;
   int64_t b, d0, d, row, row0, t_begin;
-  uint32_t steps, row_bytes, ch_off, lane_off;
+  uint32_t steps, row_bytes, ch_off, lane_off, bc_row;
   unsigned tile;
   int s, wv;
   bool active;
@@ -239,10 +240,13 @@ struct TileCtx {
     ch_off = active ? tid * eb : kOffNone;
     lane_off = CW != 0 ? tile_lane_offset<IO, (CW != 0 ? CW : 4)>(row_bytes, valid_bytes) : 0u;
     wv = __builtin_amdgcn_readfirstlane(tid / 64);
-    Bp = static_cast<const raw*>(B) + (b * g.seqlen + t_begin) * N;
-    Cp = static_cast<const raw*>(C) + (b * g.seqlen + t_begin) * N;
+    // the tile's group of B and C (every channel of a tile is in one group)
+    const int64_t grp = d0 / g.group_dim;
+    bc_row = static_cast<uint32_t>(g.ngroups * N);
+    Bp = static_cast<const raw*>(B) + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
+    Cp = static_cast<const raw*>(C) + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
 #pragma unroll
-    for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock);
+    for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock, bc_row);
   }
 
   // Start copying the tile rows of chunk step t1 of `count` tensors into the
@@ -275,8 +279,8 @@ struct TileCtx {
   __device__ __forceinline__ void fetch_bc(uint32_t t1, float (&bcv)[kBcPer]) const {
 #pragma unroll
     for (int r = 0; r < kBcPer; ++r)
-      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
-                              steps - t1, bco[r]);
+      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * bc_row,
+                              Cp + static_cast<int64_t>(t1) * bc_row, steps - t1, bco[r], bc_row);
   }
   __device__ __forceinline__ void land_bc(const float (&bcv)[kBcPer], float (*bc)[2 * N]) const {
 #pragma unroll
@@ -839,22 +843,27 @@ __global__ __launch_bounds__(kAuxBlock) void bwd_param_sum_kernel(const float* _
   }
 }
 
-// dB[b, t, n] = sum over channel tiles of pBC[tile, b, t, n], dC from n + N.
+// dB[b, t, g, n] = sum over the channel tiles of group g of pBC[tile, b, t, n],
+// dC from n + N (tiles_per_group consecutive tiles per group).
 template <int N>
 __global__ __launch_bounds__(kAuxBlock) void bwd_bc_sum_kernel(const float* __restrict__ pBC,
                                                             float* __restrict__ dB,
                                                             float* __restrict__ dC,
-                                                            int64_t tokens, unsigned tiles) {
+                                                            int64_t tokens, int64_t ngroups,
+                                                            unsigned tiles_per_group) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kAuxBlock + threadIdx.x;
-  const int64_t total = tokens * 2 * N;
+  const int64_t total = tokens * ngroups * 2 * N;
   if (i >= total) return;
-  const float acc = strided_sum(pBC + i, total, tiles);
-  const int64_t tok = i / (2 * N);
   const int k = static_cast<int>(i % (2 * N));
+  const int64_t tg = i / (2 * N);  // token * ngroups + group
+  const int64_t tok = tg / ngroups, grp = tg % ngroups;
+  const int64_t tile_stride = tokens * 2 * N;  // one tile's partials
+  const float acc = strided_sum(pBC + grp * tiles_per_group * tile_stride + tok * 2 * N + k,
+                                tile_stride, tiles_per_group);
   if (k < N)
-    dB[tok * N + k] = acc;
+    dB[tg * N + k] = acc;
   else
-    dC[tok * N + k - N] = acc;
+    dC[tg * N + k - N] = acc;
 }
 
 // dst[i] = src[i], or 0 without src.
@@ -884,6 +893,8 @@ hipError_t launch_typed(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* 
   g.seg_len = plan.seg.seg_len;
   g.segments = plan.seg.segments;
   g.tiles = static_cast<unsigned>((p.dim + kBlock - 1) / kBlock);
+  g.ngroups = p.ngroups;
+  g.group_dim = p.dim / p.ngroups;
   BwdPtrs a;
   a.x = p.x;
   a.delta = p.delta;
@@ -940,10 +951,11 @@ hipError_t launch_typed(const ScanBwdProblem& p, const ScanBwdPlan& plan, char* 
                      dim3(kAuxBlock), 0, stream, a.pA, a.pDb, p.dA, p.dD, p.dbias, p.dim,
                      static_cast<int64_t>(g.segments) * p.batch);
   const int64_t tokens = p.batch * p.seqlen;
-  const int64_t nbc = tokens * 2 * N;
+  const int64_t nbc = tokens * p.ngroups * 2 * N;
   hipLaunchKernelGGL((bwd_bc_sum_kernel<N>),
                      dim3(static_cast<unsigned>((nbc + kAuxBlock - 1) / kAuxBlock)),
-                     dim3(kAuxBlock), 0, stream, a.pBC, p.dB, p.dC, tokens, g.tiles);
+                     dim3(kAuxBlock), 0, stream, a.pBC, p.dB, p.dC, tokens, p.ngroups,
+                     static_cast<unsigned>(g.tiles / p.ngroups));
   return hipGetLastError();
 }
 

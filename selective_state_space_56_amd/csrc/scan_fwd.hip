@@ -40,6 +40,8 @@ struct Dims {
   unsigned tiles;   // channel tiles of kBlock per batch row
   uint32_t* tile_flags;  // per channel tile: 1 = S4D-Real shaped (workspace), or null
   const float* h0;       // state before the first step, (batch, dim, N), or null (zeros)
+  int64_t ngroups;       // B and C groups: (batch, seqlen, ngroups, N)
+  int64_t group_dim;     // channels per group (a multiple of kBlock when ngroups > 1)
 };
 
 enum Mode { kOutput = 0, kAggregate = 1 };
@@ -276,12 +278,15 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const raw* dl0 = delta + row0;
   const raw* z0 = kZ ? z + row0 : x + row0;
   raw* out0 = out + row0;
-  const raw* Bp = B + (b * g.seqlen + t_begin) * N;
-  const raw* Cp = C + (b * g.seqlen + t_begin) * N;
+  // the tile's group of B and C (every channel of a tile is in one group)
+  const int64_t grp = d0 / g.group_dim;
+  const uint32_t bc_row = static_cast<uint32_t>(g.ngroups * N);  // elements per step
+  const raw* Bp = B + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
+  const raw* Cp = C + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
   // this thread's B/C tile elements: tid, tid + kBlock, ...
   BcOffsets bco[kBcPer];
 #pragma unroll
-  for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock);
+  for (int r = 0; r < kBcPer; ++r) bco[r] = bc_offsets<N, IO>(tid + r * kBlock, bc_row);
 
   float S = 0.0f, S_c = 0.0f;  // Kahan-compensated sum of Delta (aggregate mode)
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
@@ -305,8 +310,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   auto fetch_bc = [&](uint32_t t1) {
 #pragma unroll
     for (int r = 0; r < kBcPer; ++r)
-      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * N, Cp + static_cast<int64_t>(t1) * N,
-                              steps - t1, bco[r]);
+      bcv[r] = bc_elem<N, IO>(Bp + static_cast<int64_t>(t1) * bc_row,
+                              Cp + static_cast<int64_t>(t1) * bc_row, steps - t1, bco[r], bc_row);
   };
   auto land_bc = [&](int nb) {
 #pragma unroll
@@ -494,6 +499,8 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.segments = plan.segments;
   g.tiles = static_cast<unsigned>((p.dim + kBlock - 1) / kBlock);
   g.h0 = p.h0;
+  g.ngroups = p.ngroups;
+  g.group_dim = p.dim / p.ngroups;
   float* ws_h = static_cast<float*>(workspace);
   float* ws_s = ws_h ? ws_h + static_cast<int64_t>(plan.segments - 1) * g.rows * N : nullptr;
   g.tile_flags = ws_s ? reinterpret_cast<uint32_t*>(ws_s + static_cast<int64_t>(plan.segments - 1) *

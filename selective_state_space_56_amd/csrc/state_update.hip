@@ -40,6 +40,8 @@ struct DecodeKernelArgs {
   void* out;
   int64_t batch;
   int64_t dim;
+  int64_t ngroups;    // B and C: (batch, ngroups, N)
+  int64_t group_dim;  // channels per group
 };
 
 // Grid: x = (channel, lane-of-row) pairs, kBlock per workgroup; y = runs of
@@ -91,8 +93,9 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a
 #pragma unroll
         for (int k = 0; k < SPL; ++k) h[r][k] = hp[k];
       }
-      const raw* Bt = static_cast<const raw*>(a.B) + b * N + sub * SPL;
-      const raw* Ct = static_cast<const raw*>(a.C) + b * N + sub * SPL;
+      const int64_t bg = (b * a.ngroups + d / a.group_dim) * N;  // (b, group of d)
+      const raw* Bt = static_cast<const raw*>(a.B) + bg + sub * SPL;
+      const raw* Ct = static_cast<const raw*>(a.C) + bg + sub * SPL;
 #pragma unroll
       for (int k = 0; k < SPL; ++k) {
         Bv[r][k] = IO::load(Bt + k);
@@ -151,6 +154,8 @@ hipError_t launch_typed(const DecodeProblem& p, hipStream_t stream) {
   a.out = p.out;
   a.batch = p.batch;
   a.dim = p.dim;
+  a.ngroups = p.ngroups;
+  a.group_dim = p.dim / p.ngroups;
   const int64_t threads = p.dim * LPR;
   const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock),
                   static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));

@@ -141,17 +141,18 @@ __device__ __forceinline__ void store_tile_regs(const TileRegs<IO>& tr, typename
 
 // Thread i < kChunk * 2N fetches element i of a chunk's B/C tile: B or C of
 // step i / 2N, state i % 2N (C when i % 2N >= N). Its byte offsets into B and
-// into C (kOffNone for the tensor it does not read, and for i past the tile):
+// into C (kOffNone for the tensor it does not read, and for i past the tile);
+// consecutive steps are row_elems elements apart (G * N with G groups).
 struct BcOffsets {
   uint32_t b, c;
 };
 template <int N, class IO>
-__device__ __forceinline__ BcOffsets bc_offsets(int i) {
+__device__ __forceinline__ BcOffsets bc_offsets(int i, uint32_t row_elems) {
   constexpr int eb = sizeof(typename IO::raw);
   const int j = i / (2 * N), k = i % (2 * N);
   const bool in_tile = i < kChunk * 2 * N;
-  return {in_tile && k < N ? static_cast<uint32_t>((j * N + k) * eb) : kOffNone,
-          in_tile && k >= N ? static_cast<uint32_t>((j * N + k - N) * eb) : kOffNone};
+  return {in_tile && k < N ? static_cast<uint32_t>((j * row_elems + k) * eb) : kOffNone,
+          in_tile && k >= N ? static_cast<uint32_t>((j * row_elems + k - N) * eb) : kOffNone};
 }
 
 // This thread's B/C tile element for the chunk whose first step is row 0 of
@@ -159,9 +160,9 @@ __device__ __forceinline__ BcOffsets bc_offsets(int i) {
 // never used), widened to fp32.
 template <int N, class IO>
 __device__ __forceinline__ float bc_elem(const typename IO::raw* Bc, const typename IO::raw* Cc,
-                                         uint32_t rows_left, BcOffsets o) {
+                                         uint32_t rows_left, BcOffsets o, uint32_t row_elems) {
   constexpr int eb = sizeof(typename IO::raw);
-  const uint32_t bytes = rows_left * N * eb;
+  const uint32_t bytes = rows_left * row_elems * eb;
   const auto rb = make_rsrc(Bc, bytes), rc = make_rsrc(Cc, bytes);
   return IO::to_f32(IO::bit_or(IO::bload(rb, o.b, 0), IO::bload(rc, o.c, 0)));
 }

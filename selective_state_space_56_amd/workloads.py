@@ -178,6 +178,16 @@ def make_decode_token(w: Workload, step: int, device="cpu", seed=0):
             "z": None if z is None else z.to(io)}
 
 
+def make_grouped_bc(w: Workload, ngroups: int, device="cpu", seed=0, decode=False):
+    """B and C ~ N(0, 1) for ngroups groups of channels: (batch, L, G, N), or
+    (batch, G, N) for one decode token, in the io dtype."""
+    g = _gen(device, seed * 31337 + 11)
+    shp = (w.batch, ngroups, w.dstate) if decode else (w.batch, w.seqlen, ngroups, w.dstate)
+    B = torch.randn(shp, generator=g, device=device).to(w.torch_io)
+    C = torch.randn(shp, generator=g, device=device).to(w.torch_io)
+    return B, C
+
+
 def make_bwd_grads(w: Workload, device="cpu", seed=0):
     """Incoming gradients for the backward pass: dout ~ N(0, 1) (batch, L, dim)
     in the io dtype, and dlast ~ N(0, 1) (batch, dim, N) fp32 for the final

@@ -320,3 +320,29 @@ def test_zoh_flag_validation(lib):
     need = lib.mamba_scan_bwd_workspace_size(ctypes.byref(d))
     assert bwd(lib, dz_, ws=40, ws_bytes=need) == UNSUPPORTED
     assert "ZOH" in err(lib)
+
+
+def test_groups_validation(lib):
+    """ngroups must divide dim; the full-sequence entry points need whole
+    256-channel tiles per group; decode takes any divisor."""
+    bad = D_(batch=1, seqlen=8, dim=640)
+    bad.ngroups = 3                                   # 640 % 3 != 0
+    assert scan(lib, bad) == INVALID
+    assert "not a multiple of ngroups" in err(lib)
+    part = D_(batch=1, seqlen=8, dim=640)
+    part.ngroups = 2                                  # 320 channels per group
+    assert scan(lib, part) == UNSUPPORTED
+    assert "multiple of 256" in err(lib)
+    assert lib.mamba_scan_workspace_size(ctypes.byref(part)) == 0
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(part)) == 0
+    assert bwd(lib, part, ws=40, ws_bytes=1 << 20) == UNSUPPORTED
+    neg = D_(batch=1, seqlen=8, dim=512)
+    neg.ngroups = -1
+    assert scan(lib, neg) == INVALID
+    dec = D_(batch=1, seqlen=1, dim=640)
+    dec.ngroups = 3
+    assert upd(lib, dec) == INVALID                   # still must divide dim
+    ok = D_(batch=1, seqlen=64, dim=512)
+    ok.ngroups = 2
+    one = D_(batch=1, seqlen=64, dim=512)
+    assert lib.mamba_scan_workspace_size(ctypes.byref(ok)) == lib.mamba_scan_workspace_size(ctypes.byref(one))
