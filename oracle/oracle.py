@@ -64,6 +64,8 @@ class Oracle:
         lib.oracle_state_update_f64.argtypes = [_i64] * 4 + [_dp] * 9 + [ctypes.c_int, _dp, ctypes.c_int]
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_scan_bwd_f64.argtypes = [_i64] * 5 + [_dp] * 20 + [ctypes.c_int]
+        lib.oracle_ssd_f64.restype = ctypes.c_int
+        lib.oracle_ssd_f64.argtypes = [_i64] * 6 + [_dp] * 10 + [ctypes.c_int]
         lib.oracle_conv1d_silu_f64.restype = ctypes.c_int
         lib.oracle_conv1d_silu_f64.argtypes = [_i64] * 4 + [_dp] * 6 + [ctypes.c_int]
         lib.oracle_conv1d_update_f64.restype = ctypes.c_int
@@ -158,6 +160,30 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_bwd_f64 returned %d" % rc)
         return g
+
+    def ssd(self, x, dt, A, B, C, D=None, dt_bias=None, h0=None, nthreads=None):
+        """Mamba-2 SSD layer by its recurrence. x: (batch, L, H, P); dt: (batch,
+        L, H); A, D, dt_bias: (H,); B, C: (batch, L, G, N); h0: (batch, H, N,
+        P). Returns (out (batch, L, H, P), last_state (batch, H, N, P)), fp64."""
+        x = _f64(x)
+        batch, L, H, P = x.shape
+        dt = _f64(dt, (batch, L, H))
+        A = _f64(A, (H,))
+        G, N = np.asarray(B).shape[2], np.asarray(B).shape[3]
+        B = _f64(B, (batch, L, G, N))
+        C = _f64(C, (batch, L, G, N))
+        D = _f64(D, (H,))
+        dt_bias = _f64(dt_bias, (H,))
+        h0 = _f64(h0, (batch, H, N, P))
+        out = np.empty((batch, L, H, P))
+        last = np.empty((batch, H, N, P))
+        nt = nthreads if nthreads else (os.cpu_count() or 1)
+        rc = self.lib.oracle_ssd_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(out),
+                                     _ptr(last), nt)
+        if rc != 0:
+            raise ValueError("oracle_ssd_f64 returned %d" % rc)
+        return out, last
 
     def conv1d(self, xin, weight, bias=None, state_in=None, nthreads=None):
         """Causal depthwise convolution + SiLU. xin: (batch, L, dim); weight:

@@ -374,3 +374,63 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t seqlen, int64_t dim, int64_t dsta
   free(hist);
   return 0;
 }
+
+/*
+ * Mamba-2 state space duality (SSD) layer, by its linear recurrence
+ * (ai.thesatyajit.com, "Mamba and selective state spaces, from first
+ * principles", section "Mamba-2: state space duality"): A_t is a scalar times
+ * the identity, a_t = exp(Delta_t A_h) with one A_h per head; the channels form
+ * heads of P channels that share a_t, B_t and C_t, and each head's state is an
+ * N x P matrix. Written, like the S6 layer above, with the first-order input
+ * weight and the softplus(Delta_raw + bias) step:
+ *
+ *   Delta_t = softplus(dt[b,t,h] + dt_bias[h])
+ *   S_t     = exp(Delta_t A[h]) S_{t-1} + Delta_t B_t x_t^T     (N x P)
+ *   y_t     = S_t^T C_t + D[h] x_t                              (P)
+ *
+ * with S_{-1} = h0 (or 0). Heads form ngroups equal consecutive groups; head h
+ * reads the B and C of group h / (nheads / ngroups).
+ * Layouts (row-major, contiguous): x, out: (batch, seqlen, nheads, headdim);
+ * dt: (batch, seqlen, nheads); A, D, dt_bias: (nheads); B, C: (batch, seqlen,
+ * ngroups, dstate); h0, last_state: (batch, nheads, dstate, headdim). D,
+ * dt_bias, h0, last_state may be NULL.
+ */
+int oracle_ssd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int64_t ngroups, const double *x, const double *dt,
+                   const double *A, const double *B, const double *C, const double *D,
+                   const double *dt_bias, const double *h0, double *out, double *last_state,
+                   int nthreads) {
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1) return -1;
+  if (ngroups < 1 || nheads % ngroups != 0) return -1;
+  if (!x || !dt || !A || !B || !C || !out) return -1;
+  if (nthreads < 1) nthreads = 1;
+  const int64_t H = nheads, P = headdim, N = dstate, G = ngroups, per_group = nheads / ngroups;
+
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      double *S = (double *)malloc(sizeof(double) * (size_t)(N * P));
+      for (int64_t k = 0; k < N * P; ++k) S[k] = h0 ? h0[(b * H + h) * N * P + k] : 0.0;
+      const int64_t g = h / per_group;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        const double Delta = softplus(dt[(b * seqlen + t) * H + h] + (dt_bias ? dt_bias[h] : 0.0));
+        const double a = exp(Delta * A[h]);
+        const double *Bt = B + ((b * seqlen + t) * G + g) * N;
+        const double *Ct = C + ((b * seqlen + t) * G + g) * N;
+        const double *xt = x + ((b * seqlen + t) * H + h) * P;
+        double *yt = out + ((b * seqlen + t) * H + h) * P;
+        for (int64_t n = 0; n < N; ++n)
+          for (int64_t p = 0; p < P; ++p) S[n * P + p] = a * S[n * P + p] + Delta * Bt[n] * xt[p];
+        for (int64_t p = 0; p < P; ++p) {
+          double y = D ? D[h] * xt[p] : 0.0;
+          for (int64_t n = 0; n < N; ++n) y += Ct[n] * S[n * P + p];
+          yt[p] = y;
+        }
+      }
+      if (last_state)
+        for (int64_t k = 0; k < N * P; ++k) last_state[(b * H + h) * N * P + k] = S[k];
+      free(S);
+    }
+  }
+  return 0;
+}

@@ -601,6 +601,63 @@ BWD_PINS = [pin_bwd_finite_differences, pin_bwd_finite_differences_bare, pin_bwd
 
 
 # ---------------------------------------------------------------------------
+# Mamba-2 SSD (ai.thesatyajit.com, "Mamba and selective state spaces, from
+# first principles", section "Mamba-2: state space duality")
+# ---------------------------------------------------------------------------
+
+def _ssd_problem(seed, batch=2, L=11, H=4, P=3, N=5, G=2):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.normal(size=(batch, L, H, P)), dt=rng.normal(size=(batch, L, H)),
+                A=-rng.uniform(0.2, 2, H), B=rng.normal(size=(batch, L, G, N)),
+                C=rng.normal(size=(batch, L, G, N)), D=rng.normal(size=H),
+                dt_bias=rng.normal(0, .5, H), h0=rng.normal(size=(batch, H, N, P)))
+
+
+def pin_ssd_is_s6_with_scalar_decay(orc):
+    """SSD is the S6 layer whose states all decay at their head's rate: the S6
+    oracle on H * P channels, with A[d, n] = A_h for every n, the head's
+    Delta_raw, bias and D on each of its channels, and B, C in groups of
+    heads, gives the same outputs and states (the S6 state h[d, n] of channel
+    d = h * P + p is S[h][n, p])."""
+    q = _ssd_problem(61)
+    batch, L, H, P = q["x"].shape
+    N = q["B"].shape[3]
+    y, last = orc.ssd(q["x"], q["dt"], q["A"], q["B"], q["C"], D=q["D"], dt_bias=q["dt_bias"],
+                      h0=q["h0"])
+    rep = lambda v: np.repeat(v, P, axis=-1)
+    y6, last6 = orc.scan(q["x"].reshape(batch, L, H * P), rep(q["dt"]),
+                         np.repeat(q["A"], P)[:, None] * np.ones((1, N)), q["B"], q["C"],
+                         D=rep(q["D"]), delta_bias=rep(q["dt_bias"]),
+                         h0=q["h0"].transpose(0, 1, 3, 2).reshape(batch, H * P, N))
+    _close(y.reshape(batch, L, H * P), y6, 1e-13, 1e-15, "SSD = S6 with scalar decay (y)")
+    _close(last.transpose(0, 1, 3, 2).reshape(batch, H * P, N), last6, 1e-13, 1e-15,
+           "SSD = S6 with scalar decay (state)")
+
+
+def pin_ssd_dual_form(orc):
+    """Unrolled, the layer is one masked matrix product (the duality): with C
+    as queries, B as keys and Delta x as values, y = (L o C B^T)(Delta x) +
+    D x, where L[t, s] = exp(A_h sum_{u=s+1..t} Delta_u) on and below the
+    diagonal and 0 above it (a decay mask in place of the softmax)."""
+    q = _ssd_problem(62)
+    batch, L, H, P = q["x"].shape
+    G = q["B"].shape[2]
+    y, _ = orc.ssd(q["x"], q["dt"], q["A"], q["B"], q["C"], D=q["D"], dt_bias=q["dt_bias"])
+    for b in range(batch):
+        for h in range(H):
+            g = h // (H // G)
+            Dl = np.logaddexp(0.0, q["dt"][b, :, h] + q["dt_bias"][h])   # softplus
+            cum = np.cumsum(Dl * q["A"][h])
+            mask = np.tril(np.exp(cum[:, None] - cum[None, :]))
+            scores = q["C"][b, :, g] @ q["B"][b, :, g].T
+            want = (mask * scores) @ (Dl[:, None] * q["x"][b, :, h]) + q["D"][h] * q["x"][b, :, h]
+            _close(y[b, :, h], want, 1e-12, 1e-14, f"SSD dual form b={b} h={h}")
+
+
+SSD_PINS = [pin_ssd_is_s6_with_scalar_decay, pin_ssd_dual_form]
+
+
+# ---------------------------------------------------------------------------
 # Causal depthwise convolution + SiLU (the SSM branch's front-end:
 # ai.thesatyajit.com, "The Mamba block"; erikxu.me notes, "Mamba")
 # ---------------------------------------------------------------------------
@@ -700,7 +757,7 @@ CONV_PINS = [
 ]
 
 
-ALL_PINS = [
+ALL_PINS = SSD_PINS + [
     pin_worked_example,
     pin_gated_rnn,
     pin_lti_convolution,

@@ -64,6 +64,11 @@ MUTATIONS = [
     ("bwd_group_index",
      "const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d / per_group) * N;\n        const double u",
      "const int64_t i = (b * L + t) * dim + d, j = ((b * L + t) * G + d % G) * N;\n        const double u"),
+    ("ssd_input_without_delta", "S[n * P + p] = a * S[n * P + p] + Delta * Bt[n] * xt[p];",
+     "S[n * P + p] = a * S[n * P + p] + Bt[n] * xt[p];"),
+    ("ssd_head_group", "const int64_t g = h / per_group;", "const int64_t g = h % G;"),
+    ("ssd_readout_B", "y += Ct[n] * S[n * P + p];", "y += Bt[n] * S[n * P + p];"),
+    ("ssd_decay_sign", "const double a = exp(Delta * A[h]);", "const double a = exp(-Delta * A[h]);"),
     ("bwd_dz_silu_grad", "dz[i] = dout[i] * s * sg * (1.0 + z[i] * (1.0 - sg));",
      "dz[i] = dout[i] * s * sg;"),
     ("bwd_dlast_dropped", "lam[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
