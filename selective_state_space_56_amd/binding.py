@@ -40,6 +40,12 @@ def _groups(B, time_axis=True):
     return B.shape[-2] if B.dim() == (4 if time_axis else 3) else 1
 
 
+class SsdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 class ConvDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("width", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
@@ -84,6 +90,11 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_conv1d_fwd.argtypes = [ctypes.POINTER(ConvDesc), vp, fp, fp, vp, vp, vp, vp]
         lib.mamba_conv1d_update.restype = ctypes.c_int
         lib.mamba_conv1d_update.argtypes = [ctypes.POINTER(ConvDesc), vp, vp, fp, fp, vp, vp]
+        lib.mamba_ssd_workspace_size.restype = sz
+        lib.mamba_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDesc)]
+        lib.mamba_ssd_fwd.restype = ctypes.c_int
+        lib.mamba_ssd_fwd.argtypes = [ctypes.POINTER(SsdDesc), vp, vp, fp, vp, vp, fp, fp, fp, vp,
+                                      fp, vp, sz, vp]
         lib.mamba_status_string.restype = ctypes.c_char_p
         lib.mamba_status_string.argtypes = [ctypes.c_int]
         lib.mamba_last_error.restype = ctypes.c_char_p
@@ -348,3 +359,42 @@ def conv1d_update(state, xin, weight, bias=None, *, out=None):
                                  _ptr(out), _stream(dev))
     _check(lib, st)
     return out
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, dt_bias=None, *, h0=None, out=None, last_state=None,
+            return_last_state=True):
+    """Mamba-2 SSD layer (mamba_ssd_fwd). x: (batch, L, H, 64) bf16; dt:
+    (batch, L, H) bf16; A, D, dt_bias: (H,) fp32; B, C: (batch, L, G, 128)
+    bf16; h0: (batch, H, 128, 64) fp32. Returns (out (batch, L, H, 64) bf16,
+    last_state (batch, H, 128, 64) fp32 or None)."""
+    lib = load_library()
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (batch, L, H, P) and B (batch, L, G, N)")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd runs on a GPU tensor")
+    bf = torch.bfloat16
+    _need(x, "x", (batch, L, H, P), bf, dev)
+    _need(dt, "dt", (batch, L, H), bf, dev)
+    _need(B, "B", (batch, L, G, N), bf, dev)
+    _need(C, "C", (batch, L, G, N), bf, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _need(h0, "h0", (batch, H, N, P), torch.float32, dev)
+    if out is None:
+        out = torch.empty((batch, L, H, P), dtype=bf, device=dev)
+    _need(out, "out", (batch, L, H, P), bf, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, H, N, P), dtype=torch.float32, device=dev)
+    _need(last_state, "last_state", (batch, H, N, P), torch.float32, dev)
+    d = SsdDesc(batch, L, H, P, N, G, _IO[bf], 0)
+    ws_bytes = int(lib.mamba_ssd_workspace_size(ctypes.byref(d)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.mamba_ssd_fwd(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(dt_bias), _ptr(h0), _ptr(out), _ptr(last_state), _ptr(ws),
+                           ctypes.c_size_t(ws_bytes), _stream(dev))
+    _check(lib, st)
+    return out, last_state

@@ -2,6 +2,7 @@
 // dispatch to the HIP kernels. See include/mamba_scan.h for the contract.
 #include "mamba_scan.h"
 #include "mamba_scan_bwd.h"
+#include "mamba_ssd.h"
 #include "mamba_conv.h"
 
 #include <hip/hip_runtime_api.h>
@@ -607,6 +608,120 @@ mamba_status mamba_scan_bwd(const mamba_scan_desc* d, const void* x, const void*
   p.io = d->io_dtype;
   p.ngroups = G;
   const hipError_t e = mscan::launch_scan_bwd(p, plan, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+mamba_status check_ssd_desc(const mamba_ssd_desc* d, const char* who) {
+  if (!d) return fail(MAMBA_ERR_INVALID_ARG, "%s: desc is NULL", who);
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 0)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: negative size", who);
+  if (d->ngroups < 1 || (d->nheads > 0 && d->nheads % d->ngroups != 0))
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: ngroups %lld must be >= 1 and divide nheads %lld", who,
+                (long long)d->ngroups, (long long)d->nheads);
+  if (d->flags != 0) return fail(MAMBA_ERR_INVALID_ARG, "%s: flags must be 0", who);
+  if (d->io_dtype != MAMBA_BF16 && d->io_dtype != MAMBA_F32)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: io_dtype %d is not a mamba_dtype", who, (int)d->io_dtype);
+  if (d->io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: only MAMBA_BF16 io is supported", who);
+  if (d->headdim != 64 || d->dstate != 128)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: headdim %lld, dstate %lld not supported (64, 128)", who,
+                (long long)d->headdim, (long long)d->dstate);
+  const int64_t lim = int64_t(1) << 40;
+  if (d->batch > 65535 || d->nheads > 65535 || d->seqlen > lim ||
+      (d->batch * d->nheads && d->seqlen > lim / (d->batch * d->nheads * 64)) ||
+      (d->seqlen + 255) / 256 > (int64_t(1) << 30))
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: problem too large", who);
+  return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_ssd_workspace_size(const mamba_ssd_desc* d) {
+  if (check_ssd_desc(d, "mamba_ssd_workspace_size") != MAMBA_OK) return 0;
+  if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
+  return mscan::ssd_workspace_bytes(d->batch, d->seqlen, d->nheads, d->ngroups);
+}
+
+mamba_status mamba_ssd_fwd(const mamba_ssd_desc* d, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const float* dt_bias,
+                           const float* h0, void* out, float* last_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const char* who = "mamba_ssd_fwd";
+  mamba_status st = check_ssd_desc(d, who);
+  if (st != MAMBA_OK) return st;
+  const int64_t H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  const int64_t tokens = d->batch * d->seqlen;
+  const int64_t elems = tokens * H * P;
+  if (d->batch == 0 || H == 0) return ok();
+  if (elems > 0) {
+    const struct {
+      const char* name;
+      const void* p;
+    } req[] = {{"x", x}, {"dt", dt}, {"A", A}, {"B", B}, {"C", C}, {"out", out}};
+    for (const auto& r : req)
+      if (!r.p) return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is NULL", who, r.name);
+  }
+  const size_t need = mamba_ssd_workspace_size(d);
+  if (elems > 0) {
+    if (!workspace)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who, need);
+    if (workspace_bytes < need)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace has %zu bytes, %zu needed", who,
+                  workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", who);
+  }
+  const Span in[] = {
+      {"x", x, static_cast<size_t>(elems) * 2},
+      {"dt", dt, static_cast<size_t>(tokens * H) * 2},
+      {"B", B, static_cast<size_t>(tokens * G * N) * 2},
+      {"C", C, static_cast<size_t>(tokens * G * N) * 2},
+      {"A", A, static_cast<size_t>(H) * 4},
+      {"D", D, static_cast<size_t>(H) * 4},
+      {"dt_bias", dt_bias, static_cast<size_t>(H) * 4},
+      {"h0", h0, static_cast<size_t>(d->batch * H * N * P) * 4},
+  };
+  const Span outs[] = {
+      {"out", out, static_cast<size_t>(elems) * 2},
+      {"last_state", last_state, static_cast<size_t>(d->batch * H * N * P) * 4},
+      {"workspace", elems > 0 ? workspace : nullptr, need},
+  };
+  for (size_t i = 0; i < 3; ++i) {
+    for (const Span& s : in)
+      if (overlaps(outs[i], s))
+        return fail(MAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", who, outs[i].name, s.name);
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(MAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", who, outs[i].name, outs[j].name);
+  }
+  if ((st = check_align(who, {in[0], in[2], in[3]}, 16)) != MAMBA_OK) return st;
+  if ((st = check_align(who, {in[1], outs[0]}, 2)) != MAMBA_OK) return st;
+  if ((st = check_align(who, {in[4], in[5], in[6], in[7], outs[1]}, 4)) != MAMBA_OK) return st;
+
+  mscan::SsdProblem p;
+  p.x = x;
+  p.dt = dt;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.dt_bias = dt_bias;
+  p.h0 = h0;
+  p.out = out;
+  p.last_state = last_state;
+  p.batch = d->batch;
+  p.seqlen = d->seqlen;
+  p.nheads = H;
+  p.ngroups = G;
+  const hipError_t e = mscan::launch_ssd_fwd(p, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

@@ -119,4 +119,22 @@ struct DecodeProblem {
 
 hipError_t launch_state_update(const DecodeProblem& p, hipStream_t stream);
 
+// Mamba-2 SSD layer (bf16 io; headdim 64, dstate 128; chunks of 256 steps).
+struct SsdProblem {
+  const void* x;        // (batch, seqlen, nheads, 64)
+  const void* dt;       // (batch, seqlen, nheads), before bias and softplus
+  const float* A;       // (nheads)
+  const void* B;        // (batch, seqlen, ngroups, 128)
+  const void* C;
+  const float* D;       // (nheads), nullable
+  const float* dt_bias; // (nheads), nullable
+  const float* h0;      // (batch, nheads, 128, 64), nullable
+  void* out;            // (batch, seqlen, nheads, 64)
+  float* last_state;    // (batch, nheads, 128, 64), nullable
+  int64_t batch, seqlen, nheads, ngroups;
+};
+
+size_t ssd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ngroups);
+hipError_t launch_ssd_fwd(const SsdProblem& p, void* workspace, hipStream_t stream);
+
 }  // namespace mscan

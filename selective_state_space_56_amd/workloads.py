@@ -188,6 +188,58 @@ def make_grouped_bc(w: Workload, ngroups: int, device="cpu", seed=0, decode=Fals
     return B, C
 
 
+@dataclass(frozen=True)
+class SsdWorkload:
+    """A Mamba-2 SSD layer: nheads heads of headdim channels, dstate states,
+    B and C in ngroups groups of heads."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int = 64
+    dstate: int = 128
+    ngroups: int = 1
+    delta_lo: float = 0.001   # softplus(dt_bias) range
+    delta_hi: float = 0.1
+    delta_std: float = 0.5    # std of dt
+
+    @property
+    def elem_steps(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+    def with_shape(self, **kw) -> "SsdWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return SsdWorkload(**d)
+
+
+SSD_WORKLOADS = {
+    # the Mamba-2 2.7B layer's heads (80 x 64 channels, N = 128, one B/C group)
+    # at the headline batch and length
+    "mamba2_2p7b_layer": SsdWorkload("mamba2_2p7b_layer", 8, 2048, 80),
+}
+
+
+def make_ssd_inputs(w: SsdWorkload, device="cpu", seed=0):
+    """x ~ N(0, 1) (batch, L, H, P); dt ~ N(0, s^2) (batch, L, H); B, C ~ N(0, 1)
+    (batch, L, G, N), all bf16; per head: dt_bias uniform in bias space between
+    softplus^-1(lo) and softplus^-1(hi), A = -exp(U(log 1, log 16)), D ~
+    U(0.5, 1.5), fp32."""
+    g = _gen(device, seed)
+    x = torch.randn((w.batch, w.seqlen, w.nheads, w.headdim), generator=g, device=device)
+    dt = torch.randn((w.batch, w.seqlen, w.nheads), generator=g, device=device) * w.delta_std
+    B = torch.randn((w.batch, w.seqlen, w.ngroups, w.dstate), generator=g, device=device)
+    C = torch.randn((w.batch, w.seqlen, w.ngroups, w.dstate), generator=g, device=device)
+    gp = _gen("cpu", seed + 7)
+    lo, hi = math.log(math.expm1(w.delta_lo)), math.log(math.expm1(w.delta_hi))
+    dt_bias = lo + (hi - lo) * torch.rand(w.nheads, generator=gp)
+    A = -torch.exp(torch.rand(w.nheads, generator=gp) * math.log(16.0))
+    D = 0.5 + torch.rand(w.nheads, generator=gp)
+    bf = torch.bfloat16
+    return {"x": x.to(bf), "dt": dt.to(bf), "B": B.to(bf), "C": C.to(bf),
+            "A": A.to(device), "D": D.to(device), "dt_bias": dt_bias.to(device)}
+
+
 def make_bwd_grads(w: Workload, device="cpu", seed=0):
     """Incoming gradients for the backward pass: dout ~ N(0, 1) (batch, L, dim)
     in the io dtype, and dlast ~ N(0, 1) (batch, dim, N) fp32 for the final

@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"mamba_scan_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_init",
                           "mamba_state_update", "mamba_status_string", "mamba_last_error",
                           "mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd",
-                          "mamba_scan_bwd_workspace_size"}
+                          "mamba_scan_bwd_workspace_size", "mamba_ssd_fwd",
+                          "mamba_ssd_workspace_size"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -346,3 +347,38 @@ def test_groups_validation(lib):
     ok.ngroups = 2
     one = D_(batch=1, seqlen=64, dim=512)
     assert lib.mamba_scan_workspace_size(ctypes.byref(ok)) == lib.mamba_scan_workspace_size(ctypes.byref(one))
+
+
+def ssd(lib, desc, ws=None, ws_bytes=0, **over):
+    names = ["x", "dt", "A", "B", "C", "D", "dt_bias", "h0", "out", "last_state"]
+    ptrs = []
+    for k, name in enumerate(names):
+        v = over.get(name, k + 1)
+        ptrs.append(None if v is None else (P(v) if isinstance(v, int) else v))
+    w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
+    return lib.mamba_ssd_fwd(None if desc is None else ctypes.byref(desc), *ptrs, w,
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_ssd_validation(lib):
+    S = lambda **kw: bd.SsdDesc(*[kw.get(k, v) for k, v in
+                                  [("batch", 1), ("seqlen", 64), ("nheads", 4), ("headdim", 64),
+                                   ("dstate", 128), ("ngroups", 1), ("io", 1), ("flags", 0)]])
+    d = S()
+    need = lib.mamba_ssd_workspace_size(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    assert ssd(lib, None) == INVALID
+    assert ssd(lib, S(headdim=32), ws=40, ws_bytes=need) == UNSUPPORTED
+    assert ssd(lib, S(dstate=64), ws=40, ws_bytes=need) == UNSUPPORTED
+    assert ssd(lib, S(io=0), ws=40, ws_bytes=need) == UNSUPPORTED
+    assert ssd(lib, S(ngroups=3), ws=40, ws_bytes=need) == INVALID
+    assert ssd(lib, S(flags=1), ws=40, ws_bytes=need) == INVALID
+    for name in ["x", "dt", "A", "B", "C", "out"]:
+        assert ssd(lib, d, ws=40, ws_bytes=need, **{name: None}) == INVALID, name
+    assert ssd(lib, d, ws=40, ws_bytes=need - 256) == INVALID
+    assert ssd(lib, d, ws=40, ws_bytes=need, out=1) == INVALID          # out == x
+    assert "overlaps" in err(lib)
+    odd = ctypes.c_void_p(FAKE + 0x100000 * 30 + 8)
+    assert ssd(lib, d, ws=40, ws_bytes=need, B=odd) == INVALID          # B needs 16 bytes
+    assert "aligned" in err(lib)
+    assert lib.mamba_ssd_workspace_size(ctypes.byref(S(headdim=32))) == 0

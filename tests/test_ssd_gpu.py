@@ -1,0 +1,90 @@
+"""GPU parity of the Mamba-2 SSD layer (mamba_ssd_fwd, through the C ABI),
+computed by the chunked matrix-core algorithm, against the oracle's plain
+recurrence on the same seeded inputs: outputs and final states."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import TOL, norm_err
+from selective_state_space_56_amd import ssd_fwd
+from selective_state_space_56_amd.workloads import SSD_WORKLOADS, make_ssd_inputs, to_f64_numpy
+
+pytestmark = pytest.mark.gpu
+
+NT = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+def _f(t):
+    return None if t is None else to_f64_numpy(t)
+
+
+def _check(orc, inp, h0=None, with_D=True, with_bias=True, heads=None, label=""):
+    D = inp["D"] if with_D else None
+    bias = inp["dt_bias"] if with_bias else None
+    out, last = ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=D, dt_bias=bias, h0=h0)
+    torch.cuda.synchronize()
+    x, dt, A = _f(inp["x"]), _f(inp["dt"]), _f(inp["A"])
+    Df, bf, h0f = _f(D), _f(bias), _f(h0)
+    got_y, got_h = to_f64_numpy(out), to_f64_numpy(last)
+    if heads is not None:   # heads are independent given their B/C group (one group here)
+        x, dt, A = x[:, :, heads], dt[:, :, heads], A[heads]
+        Df = None if Df is None else Df[heads]
+        bf = None if bf is None else bf[heads]
+        h0f = None if h0f is None else h0f[:, heads]
+        got_y, got_h = got_y[:, :, heads], got_h[:, heads]
+    ry, rh = orc.ssd(x, dt, A, _f(inp["B"]), _f(inp["C"]), D=Df, dt_bias=bf, h0=h0f, nthreads=NT)
+    ey, eh = norm_err(got_y, ry), norm_err(got_h, rh)
+    _say(f"ssd {label}: err(y)={ey:.3e} err(state)={eh:.3e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"], (ey, eh)
+
+
+@pytest.mark.parametrize("batch,L,H,G", [
+    (2, 300, 4, 1),     # two chunks, the second ragged
+    (1, 256, 3, 1),     # exactly one chunk
+    (2, 513, 4, 2),     # three chunks, two groups of heads
+    (1, 1, 2, 1),       # one step
+    (2, 1100, 2, 1),    # five chunks
+])
+def test_ssd_vs_oracle(orc, dev, batch, L, H, G):
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"].with_shape(batch=batch, seqlen=L, nheads=H, ngroups=G)
+    inp = make_ssd_inputs(w, device=dev, seed=L + H)
+    _check(orc, inp, label=f"{batch}x{L}x{H} G={G}")
+
+
+def test_ssd_optional_inputs(orc, dev):
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"].with_shape(batch=2, seqlen=400, nheads=3)
+    inp = make_ssd_inputs(w, device=dev, seed=5)
+    h0 = torch.randn((2, 3, w.dstate, w.headdim), generator=torch.Generator().manual_seed(3)).to(dev)
+    _check(orc, inp, h0=h0, label="h0")
+    _check(orc, inp, with_D=False, with_bias=False, label="no D, no bias")
+
+
+def test_ssd_empty_sequence(dev):
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"].with_shape(batch=2, seqlen=0, nheads=3)
+    inp = make_ssd_inputs(w, device=dev, seed=1)
+    h0 = torch.randn((2, 3, w.dstate, w.headdim), device=dev)
+    out, last = ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], h0=h0)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.equal(last, h0)
+
+
+def test_ssd_full_size_sampled_heads(orc, dev):
+    """The Mamba-2 2.7B layer's heads (8 x 2048, 80 heads of 64, N = 128) as the
+    benchmark launches it; the oracle follows sampled heads."""
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"]
+    inp = make_ssd_inputs(w, device=dev)
+    heads = np.array([0, 1, 41, 79])
+    _check(orc, inp, heads=heads, label="2.7B layer, sampled heads")
