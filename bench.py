@@ -16,7 +16,9 @@ state written once) against the HBM peak. `cpu_baseline` is the fp64 oracle
 timed on this host on a bounded sample of the same workload. Measured in the
 same run, each with its own roofline: the backward call on the same layer
 (`bwd`), the decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32
-state, `decode`) and the causal convolution front-end (`conv`).
+state, `decode`), the causal convolution front-end (`conv`) and the Mamba-2
+SSD layer (80 heads of 64, N = 128, 8 x 2048, `ssd`, against the bf16
+matrix-core peak).
 """
 from __future__ import annotations
 
@@ -42,7 +44,9 @@ KERNEL_SOURCES = {
     "conv": ["conv1d.hip", "device_math.h", "conv.h"],
     "conv_update": ["conv1d.hip", "device_math.h", "conv.h"],
     "bwd": ["scan_bwd.hip", "scan_fwd.hip", "tile_io.h", "device_math.h", "kernels.h"],
+    "ssd": ["ssd.hip", "device_math.h", "kernels.h"],
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def source_hash(kind: str) -> str:
@@ -119,6 +123,25 @@ def bwd_flops(w) -> int:
     silu(z) and its sigmoid (4), ds (1), dx (3), dDelta_raw (3), dz (5), the
     dD and dbias sums (3) = 25."""
     return w.batch * w.seqlen * w.dim * (22 * w.dstate + 25)
+
+
+def ssd_flops(w) -> int:
+    """Algorithmic matrix-core work of one SSD call (the chunked algorithm, FMA
+    = 2 flops), per (batch row, head, chunk of Q steps): the causal half of the
+    scores C B^T (Q^2 N), the masked scores times X (Q^2 P), the chunk state
+    (2 Q N P) and the inherited state's read-out C S_in (2 Q N P)."""
+    Q = 256
+    chunks = -(-w.seqlen // Q)
+    per = Q * Q * (w.dstate + w.headdim) + 4 * Q * w.dstate * w.headdim
+    return w.batch * w.nheads * chunks * per
+
+
+def ssd_bytes(w) -> int:
+    """Algorithmic HBM bytes of one SSD call: x read and y written (bf16), dt
+    (bf16, one per head and step), B and C (bf16, per group and step) read
+    once, A, D and bias per head."""
+    return (2 * w.batch * w.seqlen * w.nheads * w.headdim * 2 + w.batch * w.seqlen * w.nheads * 2
+            + 2 * w.batch * w.seqlen * w.ngroups * w.dstate * 2 + 3 * w.nheads * 4)
 
 
 def decode_bytes(w) -> int:
@@ -220,7 +243,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
-    ap.add_argument("--parts", default="fwd,bwd,decode,conv",
+    ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--parts", default="fwd,bwd,decode,conv,ssd",
                     help="comma list of the parts to run (profiling runs take one family at a time); "
                          "without fwd only the other parts' objects are printed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -271,6 +295,8 @@ def main():
         rec["decode"] = decode_part(stream)
     if run_conv:
         rec["conv"] = conv_part(args, w, stream)
+    if "ssd" in parts and not args.no_ssd:
+        rec["ssd"] = ssd_part(args, stream)
     if run_fwd and not args.no_cpu_baseline:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
         rec["cpu_baseline"] = cpu_baseline(w, inp, nthreads)
@@ -462,6 +488,45 @@ def conv_part(args, w, stream):
     }
     del ci, cout, cst, cd, cstate
     return out
+
+
+def ssd_part(args, stream):
+    import torch
+    from selective_state_space_56_amd import ssd_fwd
+    from selective_state_space_56_amd.workloads import SSD_WORKLOADS, make_ssd_inputs
+    dev = torch.device("cuda", 0)
+    ws = SSD_WORKLOADS["mamba2_2p7b_layer"]
+    si = make_ssd_inputs(ws, device=dev)
+    out = torch.empty_like(si["x"])
+    last = torch.empty((ws.batch, ws.nheads, ws.dstate, ws.headdim), dtype=torch.float32, device=dev)
+
+    def sstep():
+        ssd_fwd(si["x"], si["dt"], si["A"], si["B"], si["C"], D=si["D"], dt_bias=si["dt_bias"],
+                out=out, last_state=last)
+
+    for _ in range(args.warmup):
+        sstep()
+    torch.cuda.synchronize()
+    calls = time_calls(sstep, args.steps, stream)
+    ms = sum(calls) / len(calls)
+    fl, by = ssd_flops(ws), ssd_bytes(ws)
+    res = {
+        "op": "mamba_ssd_fwd (Mamba-2 SSD, chunked on the matrix cores)", "workload": ws.name,
+        "config": {"batch": ws.batch, "seq_len": ws.seqlen, "heads": ws.nheads,
+                   "head_dim": ws.headdim, "d_state": ws.dstate, "groups": ws.ngroups, "chunk": 256,
+                   "io": "bf16"},
+        "avg_launch_ms": ms, **call_stats(calls),
+        "value": ws.elem_steps / (ms * 1e-3), "unit": "elem-steps/s",
+        "roofline": {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic("ssd", ws.name),
+                     "algorithmic_flops_per_launch": fl},
+        "hbm": {"achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": by},
+    }
+    del si, out, last
+    return res
 
 
 if __name__ == "__main__":
