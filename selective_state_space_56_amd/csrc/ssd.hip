@@ -20,6 +20,9 @@
 //   B (16 x 32): lane l holds column l % 32, the same k;
 //   D (32 x 32): register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
 //                column l % 32.
+// Where k is the time step, the operands come from tiles kept in LDS in their
+// HBM order (step-major rows written with 16-byte stores) and are read with the
+// transposing LDS load of gfx950 (ds_read_b64_tr_b16), see lds_kmajor.
 #include "device_math.h"
 #include "kernels.h"
 
@@ -33,10 +36,16 @@ constexpr int kN = 128;       // state size
 constexpr int kThreads = 256; // four waves
 constexpr int kSBlk = 64;     // steps per LDS block of the chunk-state product
 constexpr int kPad = 8;       // bf16 padding of LDS rows (keeps rows 16-byte aligned, spreads banks)
+constexpr int kWidePad = 32;  // padding that puts the four rows of a transposing read on distinct banks
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -55,22 +64,36 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
 
+// The k-major MFMA operand from a row-major LDS tile T[k][col] (row stride ld
+// elements, a multiple of 4; T 8-byte aligned): lane l receives
+// T[8 (l / 32) + e][l % 32], e = 0..7, i.e. column (or row) l % 32 of the tile
+// with k-half l / 32. ds_read_b64_tr_b16 works on groups of 16 lanes: lane q
+// of a group names 4 consecutive elements of row q / 4 of a 4 x 16 block and
+// receives column q of that block; two such reads give the 8 values of k.
+__device__ __forceinline__ bf16x8 lds_kmajor(const uint16_t* T, int ld, int lane) {
+  const int grp = lane >> 4, q = lane & 15;
+  const uint16_t* p = T + (8 * (grp >> 1) + (q >> 2)) * ld + 16 * (grp & 1) + 4 * (q & 3);
+  const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+  const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p + 4 * ld));
+  const s16x8 v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 struct SsdDims {
   int64_t batch, seqlen, nheads, ngroups;
   int chunks;
 };
 
 // Delta_t = softplus(dt + bias) of the workgroup's chunk, one step per thread
-// (zero past the sequence's end), and ell_t = sum_{u <= t} Delta_u A_h, an
-// inclusive prefix sum over the chunk (wave scans, then the wave totals).
-__device__ __forceinline__ void chunk_decay(const uint16_t* __restrict__ dt, float bias, float A_h,
-                                            const SsdDims& g, int64_t b, int64_t h, int c,
-                                            float* s_delta, float* s_ell, float* s_wave) {
+// of the first kQ (zero for steps past the sequence's end: `valid` false), and
+// ell_t = sum_{u <= t} Delta_u A_h, an inclusive prefix sum over the chunk (wave
+// scans, then the wave totals). s_wave holds one value per wave of the
+// workgroup. `dt_raw` is this thread's dt value, loaded beforehand.
+__device__ __forceinline__ void chunk_decay_from(float dt_raw, bool valid, float bias, float A_h,
+                                                 float* s_delta, float* s_ell, float* s_wave) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int64_t t = static_cast<int64_t>(c) * kQ + tid;
-  float Delta = 0.0f;
-  if (t < g.seqlen) Delta = softplus_f(from_bf16(dt[(b * g.seqlen + t) * g.nheads + h]) + bias);
+  const float Delta = valid ? softplus_f(dt_raw + bias) : 0.0f;
   float v = Delta * A_h;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -81,137 +104,185 @@ __device__ __forceinline__ void chunk_decay(const uint16_t* __restrict__ dt, flo
   __syncthreads();
   float base = 0.0f;
   for (int w = 0; w < wv; ++w) base += s_wave[w];
-  s_delta[tid] = Delta;
-  s_ell[tid] = base + v;
+  if (tid < kQ) {
+    s_delta[tid] = Delta;
+    s_ell[tid] = base + v;
+  }
   __syncthreads();
 }
 
+// The dt value of this thread's step of chunk c, and whether the step lies in
+// the sequence.
+__device__ __forceinline__ float load_dt(const uint16_t* __restrict__ dt, const SsdDims& g, int64_t b,
+                                         int64_t h, int c, bool& valid) {
+  const int64_t t = static_cast<int64_t>(c) * kQ + threadIdx.x;
+  valid = threadIdx.x < kQ && t < g.seqlen;
+  return valid ? from_bf16(dt[(b * g.seqlen + t) * g.nheads + h]) : 0.0f;
+}
+
+__device__ __forceinline__ void chunk_decay(const uint16_t* __restrict__ dt, float bias, float A_h,
+                                            const SsdDims& g, int64_t b, int64_t h, int c,
+                                            float* s_delta, float* s_ell, float* s_wave) {
+  bool valid;
+  const float raw = load_dt(dt, g, b, h, c, valid);
+  chunk_decay_from(raw, valid, bias, A_h, s_delta, s_ell, s_wave);
+}
+
 // ---------------------------------------------------------------------------
-// 1. Chunk states. Grid (chunks, heads, batch). S_c[p][n] (fp32, [b][h][c][p][n])
-// = sum_s w_s x_s[p] B_s[n], w_s = exp(ell_end - ell_s) Delta_s, as the product
-// of (w o X)^T (P x Q) and B (Q x N), K = s. Both operands are transposed
-// through LDS (s contiguous) one block of kSBlk steps at a time; w x is kept
-// as a bf16 pair hi + lo (two products), so the weights lose no precision to
-// the bf16 operands. Wave w owns the 32 states n of tile w and both
-// 32-channel tiles of p.
-__global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(
+// 1. Chunk states and their hand-off. Grid (heads, batch): one workgroup walks
+// the chunks of one (batch, head) in order and keeps the state S (N x P, fp32)
+// in registers. For chunk c it writes S_in(c) = S (fp32, [b][h][c][p][n]) for
+// the chunk scan, forms the chunk's own contribution
+//   S_c[p][n] = sum_s w_s x_s[p] B_s[n],   w_s = exp(ell_end - ell_s) Delta_s,
+// as the product of (w o X)^T (P x Q) and B (Q x N), K = s, and passes the state
+// on: S = exp(ell_end) S + S_c (ell_end: the chunk's total of Delta A_h). One
+// block of kSBlk steps at a time, w x (as a bf16 pair hi + lo, two products, so
+// the weights lose no precision to the bf16 operands) and B are stored
+// step-major in LDS with 16-byte writes and read k-major by transposing loads;
+// the next block's loads, and the next chunk's dt, are in flight meanwhile.
+// Wave w owns the 32 states n of tile w and both 32-channel tiles of p. The
+// final state (fp32, [b][h][n][p]) is written if asked for. No state of the
+// sequence is passed between workgroups.
+__global__ __launch_bounds__(kThreads, 3) void ssd_chunk_state_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
-    const uint16_t* __restrict__ B, const float* __restrict__ dt_bias, float* __restrict__ Sc,
-    float* __restrict__ ell_end, SsdDims g) {
-  __shared__ float s_delta[kQ], s_ell[kQ], s_wave[4];
-  __shared__ __align__(16) uint16_t s_xh[kP][kSBlk + kPad];  // (w o X)^T block, hi part
-  __shared__ __align__(16) uint16_t s_xl[kP][kSBlk + kPad];  // lo part
-  __shared__ __align__(16) uint16_t s_b[kN][kSBlk + kPad];   // B^T block
-  const int c = blockIdx.x;
-  const int64_t h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint16_t* __restrict__ B, const float* __restrict__ dt_bias, const float* __restrict__ h0,
+    float* __restrict__ Sin, float* __restrict__ last_state, SsdDims g) {
+  constexpr int ldx = kP + kWidePad, ldb = kN + kWidePad;
+  constexpr int kBlocks = kQ / kSBlk;
+  constexpr int kXP = kSBlk * kP / 8 / kThreads, kBP = kSBlk * kN / 8 / kThreads;
+  constexpr int64_t per_head = static_cast<int64_t>(kP) * kN;
+  __shared__ float s_delta[kQ], s_ell[kQ], s_wave[kThreads / 64];
+  __shared__ __align__(16) uint16_t s_xh[kSBlk][ldx];  // w o X block, hi part, [s][p]
+  __shared__ __align__(16) uint16_t s_xl[kSBlk][ldx];  // lo part
+  __shared__ __align__(16) uint16_t s_b[kSBlk][ldb];   // B block, [s][n]
+  const int64_t h = blockIdx.x, b = blockIdx.y;
+  const int64_t bh = b * g.nheads + h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lo = lane & 31, hi = lane >> 5;
   const int64_t grp = h / (g.nheads / g.ngroups);
-  chunk_decay(dt, dt_bias ? dt_bias[h] : 0.0f, A[h], g, b, h, c, s_delta, s_ell, s_wave);
-  const float ell_last = s_ell[kQ - 1];
+  const float bias = dt_bias ? dt_bias[h] : 0.0f, A_h = A[h];
+  // register r of tile pt holds S[p][n], p = 32 pt + 8 (r / 4) + 4 hi + r % 4, n = 32 wv + lo
+  auto p_of = [&](int pt, int r) { return pt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3); };
+  const int n = wv * 32 + lo;
+  f32x16 S[2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      S[pt][r] = h0 ? h0[bh * per_head + static_cast<int64_t>(n) * kP + p_of(pt, r)] : 0.0f;
 
-  f32x16 acc[2] = {};
-  for (int s0 = 0; s0 < kQ; s0 += kSBlk) {
-    // stage: thread -> step s0 + tid / 4, a quarter of its channels / states
+  // block k of chunk c into registers, 16-byte pieces with whole rows per group
+  // of lanes: X rows (8 pieces), B rows (16 pieces); rows past the sequence's
+  // end load its last row (no branch) and their B is zeroed (their weight is 0)
+  u16x8 xv[kXP], bv[kBP];
+  auto load_block = [&](int c, int k) {
+#pragma unroll
+    for (int q = 0; q < kXP; ++q) {
+      const int id = tid + kThreads * q;
+      const int64_t t = static_cast<int64_t>(c) * kQ + k * kSBlk + (id >> 3);
+      const int64_t tr = t < g.seqlen ? t : g.seqlen - 1;
+      xv[q] = *reinterpret_cast<const u16x8*>(x + ((b * g.seqlen + tr) * g.nheads + h) * kP + 8 * (id & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < kBP; ++q) {
+      const int id = tid + kThreads * q;
+      const int64_t t = static_cast<int64_t>(c) * kQ + k * kSBlk + (id >> 4);
+      const int64_t tr = t < g.seqlen ? t : g.seqlen - 1;
+      const u16x8 v = *reinterpret_cast<const u16x8*>(
+          B + ((b * g.seqlen + tr) * g.ngroups + grp) * kN + 8 * (id & 15));
+      bv[q] = t < g.seqlen ? v : u16x8{};
+    }
+  };
+  bool dt_valid = false;
+  float dt_raw = 0.0f;
+  if (g.chunks > 0) {
+    load_block(0, 0);
+    dt_raw = load_dt(dt, g, b, h, 0, dt_valid);
+  }
+  for (int c = 0; c < g.chunks; ++c) {
+    chunk_decay_from(dt_raw, dt_valid, bias, A_h, s_delta, s_ell, s_wave);
+    if (c + 1 < g.chunks) dt_raw = load_dt(dt, g, b, h, c + 1, dt_valid);
+    const float ell_last = s_ell[kQ - 1];
+    // the state entering this chunk (the row offset of register r is a constant)
     {
-      const int sl = tid >> 2, part = tid & 3;
-      const int64_t t = static_cast<int64_t>(c) * kQ + s0 + sl;
-      const bool in = t < g.seqlen;
-      const float w = in ? hw_exp2((ell_last - s_ell[s0 + sl]) * kLog2e) * s_delta[s0 + sl] : 0.0f;
-      u16x8 xv[2] = {}, bv[4] = {};
-      if (in) {
-        const u16x8* xr = reinterpret_cast<const u16x8*>(
-            x + ((b * g.seqlen + t) * g.nheads + h) * kP + part * 16);
-        const u16x8* br = reinterpret_cast<const u16x8*>(
-            B + ((b * g.seqlen + t) * g.ngroups + grp) * kN + part * 32);
-        xv[0] = xr[0];
-        xv[1] = xr[1];
+      const auto rs = make_rsrc(Sin + (bh * g.chunks + c) * per_head, per_head * 4);
+      const uint32_t voff = static_cast<uint32_t>((4 * hi * kN + n) * 4);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bv[q] = br[q];
-      }
+      for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float v = from_bf16(xv[k / 8][k % 8]) * w;
-        const uint16_t vh = to_bf16(v);
-        s_xh[part * 16 + k][sl] = vh;
-        s_xl[part * 16 + k][sl] = to_bf16(v - from_bf16(vh));
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k) s_b[part * 32 + k][sl] = bv[k / 8][k % 8];
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[pt][r]), rs, voff,
+                                                (pt * 32 + 8 * (r >> 2) + (r & 3)) * kN * 4, 0);
     }
-    __syncthreads();
+    f32x16 acc[2] = {};
 #pragma unroll
-    for (int kk = 0; kk < kSBlk; kk += 16) {
-      const int kofs = kk + 8 * (lane >> 5);
-      const bf16x8 bop = load8(&s_b[wv * 32 + (lane & 31)][kofs]);
+    for (int k = 0; k < kBlocks; ++k) {
+      // stage block k (w o X as hi + lo, B) into LDS
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        acc[pt] = mfma(load8(&s_xh[pt * 32 + (lane & 31)][kofs]), bop, acc[pt]);
-        acc[pt] = mfma(load8(&s_xl[pt * 32 + (lane & 31)][kofs]), bop, acc[pt]);
+      for (int q = 0; q < kXP; ++q) {
+        const int id = tid + kThreads * q, row = id >> 3;
+        const int64_t t = static_cast<int64_t>(c) * kQ + k * kSBlk + row;
+        const float w = t < g.seqlen
+                            ? hw_exp2((ell_last - s_ell[k * kSBlk + row]) * kLog2e) * s_delta[k * kSBlk + row]
+                            : 0.0f;
+        u16x8 vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = from_bf16(xv[q][e]) * w;
+          vh[e] = to_bf16(v);
+          vl[e] = to_bf16(v - from_bf16(vh[e]));
+        }
+        *reinterpret_cast<u16x8*>(&s_xh[row][8 * (id & 7)]) = vh;
+        *reinterpret_cast<u16x8*>(&s_xl[row][8 * (id & 7)]) = vl;
       }
+#pragma unroll
+      for (int q = 0; q < kBP; ++q) {
+        const int id = tid + kThreads * q;
+        *reinterpret_cast<u16x8*>(&s_b[id >> 4][8 * (id & 15)]) = bv[q];
+      }
+      // the next block's loads go out before this block's products
+      if (k + 1 < kBlocks)
+        load_block(c, k + 1);
+      else if (c + 1 < g.chunks)
+        load_block(c + 1, 0);
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kSBlk; kk += 16) {
+        const bf16x8 bop = lds_kmajor(&s_b[kk][wv * 32], ldb, lane);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          acc[pt] = mfma(lds_kmajor(&s_xh[kk][pt * 32], ldx, lane), bop, acc[pt]);
+          acc[pt] = mfma(lds_kmajor(&s_xl[kk][pt * 32], ldx, lane), bop, acc[pt]);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    const float decay = hw_exp2(ell_last * kLog2e);
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[pt][r] = fmaf(decay, S[pt][r], acc[pt][r]);
   }
-  float* out = Sc + (((b * g.nheads + h) * g.chunks + c) * kP) * kN;
+  if (last_state) {
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = pt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      out[p * kN + wv * 32 + (lane & 31)] = acc[pt][r];
-    }
+      for (int r = 0; r < 16; ++r)
+        last_state[bh * per_head + static_cast<int64_t>(n) * kP + p_of(pt, r)] = S[pt][r];
   }
-  if (tid == 0) ell_end[(b * g.nheads + h) * g.chunks + c] = ell_last;
 }
 
 // ---------------------------------------------------------------------------
-// 2. State pass. One thread per (b, h, p, n): the state entering each chunk,
-// S_in(0) = h0 (or 0), S_in(c + 1) = exp(ell_end(c)) S_in(c) + S_c, written as
-// a bf16 pair hi + lo, [b][h][c][p][n] each (the operand layout of the chunk
-// scan); the final state (fp32, [b][h][n][p]) if asked for. The chunk loads are
-// issued kPassAhead at a time.
-constexpr int kPassAhead = 8;
-
-__global__ __launch_bounds__(kThreads) void ssd_state_pass_kernel(
-    const float* __restrict__ Sc, const float* __restrict__ ell_end, const float* __restrict__ h0,
-    uint16_t* __restrict__ Sin_hi, uint16_t* __restrict__ Sin_lo, float* __restrict__ last_state,
-    SsdDims g) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per_head = static_cast<int64_t>(kP) * kN;
-  if (i >= g.batch * g.nheads * per_head) return;
-  const int64_t bh = i / per_head;
-  const int pn = static_cast<int>(i % per_head);
-  const int p = pn / kN, n = pn % kN;
-  float s = h0 ? h0[bh * per_head + static_cast<int64_t>(n) * kP + p] : 0.0f;
-  for (int c0 = 0; c0 < g.chunks; c0 += kPassAhead) {
-    float sc[kPassAhead], dec[kPassAhead];
-#pragma unroll
-    for (int u = 0; u < kPassAhead; ++u) {
-      const int c = c0 + u < g.chunks ? c0 + u : g.chunks - 1;
-      sc[u] = Sc[(bh * g.chunks + c) * per_head + pn];
-      dec[u] = ell_end[bh * g.chunks + c];
-    }
-#pragma unroll
-    for (int u = 0; u < kPassAhead; ++u) {
-      if (c0 + u < g.chunks) {
-        const int64_t slot = (bh * g.chunks + c0 + u) * per_head + pn;
-        const uint16_t hi = to_bf16(s);
-        Sin_hi[slot] = hi;
-        Sin_lo[slot] = to_bf16(s - from_bf16(hi));
-        s = fmaf(hw_exp2(dec[u] * kLog2e), s, sc[u]);
-      }
-    }
-  }
-  if (last_state) last_state[bh * per_head + static_cast<int64_t>(n) * kP + p] = s;
-}
-
-// ---------------------------------------------------------------------------
-// 3a. Chunk scores. Grid (chunks, groups, batch). The raw scores B_s . C_t of
-// a chunk do not depend on the head, so they are formed once per (batch,
-// chunk, group) for every head that shares the group: the kTiles
-// lower-triangular 32 x 32 tiles (s tile j <= t tile i), K = n, each stored in
-// the MFMA result layout (s as rows, t as columns) as [tile][register][lane]
-// fp32, so that a wave reads it back with coalesced loads.
+// 3a. Chunk scores. Grid (chunks * kTiles / 4, groups, batch), one tile per
+// wave. The raw scores B_s . C_t of a chunk do not depend on the head, so they
+// are formed once per (batch, chunk, group) for every head that shares the
+// group: the kTiles lower-triangular 32 x 32 tiles (s tile j <= t tile i),
+// K = n, each kept in the MFMA result layout (s as rows, t as columns), fp32,
+// stored as [tile][register / 4][lane][register % 4] so that a wave writes and
+// reads a tile with 16-byte accesses, 1 KB contiguous per instruction.
 constexpr int kTiles = (kQ / 32) * (kQ / 32 + 1) / 2;  // 36
+constexpr int kScoreBlocks = kTiles / 4;
 
 __device__ __forceinline__ int tile_index(int i, int j) { return i * (i + 1) / 2 + j; }
 
@@ -219,132 +290,167 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scores_kernel(const uint16
                                                                     const uint16_t* __restrict__ C,
                                                                     float* __restrict__ scores,
                                                                     SsdDims g) {
-  const int c = blockIdx.x;
+  const int c = blockIdx.x / kScoreBlocks;
+  const int tile = (blockIdx.x % kScoreBlocks) * 4 + (threadIdx.x >> 6);
   const int64_t grp = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int lo = lane & 31, hi = lane >> 5;
   const int64_t t_base = static_cast<int64_t>(c) * kQ;
+  int i = 0;
+  while (tile_index(i + 1, 0) <= tile) ++i;
+  const int j = tile - tile_index(i, 0);
   auto frag = [&](const uint16_t* T, int64_t t, int kb) -> bf16x8 {
     if (t >= g.seqlen) return bf16x8{};
     return load8(T + ((b * g.seqlen + t) * g.ngroups + grp) * kN + 16 * kb + 8 * hi);
   };
-  float* out = scores + ((b * g.chunks + c) * g.ngroups + grp) * (kTiles * 1024);
-  // wave w forms tiles w, w + 4, ... in the flat lower-triangular order
-  for (int tile = wv; tile < kTiles; tile += 4) {
-    int i = 0;
-    while (tile_index(i + 1, 0) <= tile) ++i;
-    const int j = tile - tile_index(i, 0);
-    f32x16 sc = {};
+  f32x16 sc = {};
 #pragma unroll
-    for (int kb = 0; kb < kN / 16; ++kb)
-      sc = mfma(frag(B, t_base + 32 * j + lo, kb), frag(C, t_base + 32 * i + lo, kb), sc);
+  for (int kb = 0; kb < kN / 16; ++kb)
+    sc = mfma(frag(B, t_base + 32 * j + lo, kb), frag(C, t_base + 32 * i + lo, kb), sc);
+  float* out = scores + (((b * g.chunks + c) * g.ngroups + grp) * kTiles + tile) * 1024;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(tile * 16 + r) * 64 + lane] = sc[r];
-  }
+  for (int r4 = 0; r4 < 4; ++r4)
+    *reinterpret_cast<f32x4*>(out + (r4 * 64 + lane) * 4) =
+        f32x4{sc[4 * r4], sc[4 * r4 + 1], sc[4 * r4 + 2], sc[4 * r4 + 3]};
 }
 
 // ---------------------------------------------------------------------------
-// 3. Chunk scan. Grid (chunks, heads, batch). Wave w computes the output rows
-// of the 32-step tiles w and 7 - w (the causal triangle split evenly) for both
-// 32-channel tiles of p:
-//   inherited part: C_t S_in (K = n; S_in as its bf16 pair hi + lo), rows
-//     scaled by exp(ell_t);
-//   diagonal part, per 32-step tile j <= i of earlier steps s: the chunk's
-//     scores B_s . C_t (a 32 x 32 tile with s as rows, from 3a), masked
-//     (s <= t) and scaled by exp(ell_t - ell_s) Delta_s, taken off the
-//     diagonal as exp(ell_t - ell_ref) exp(ell_ref - ell_s) Delta_s with ell_ref
-//     the value at the end of tile j (both factors at most 1; the second kept
-//     per step in LDS) and formed directly on the diagonal tile, turned into
-//     the A operand (t as rows, s as k) by exchanging
-//     register halves across the half-waves, times X (K = s, from LDS);
+// 3. Chunk scan. Grid (chunks, heads, batch), eight waves. The chunk's X
+// (step-major) and the state it inherits (S_in, split into a bf16 pair hi + lo,
+// [p][n]) are staged in LDS once per workgroup. Wave w computes the output rows of the
+// 32-step tile w for both 32-channel tiles of p:
+//   inherited part: C_t S_in (K = n; S_in as its pair hi + lo), rows scaled by
+//     exp(ell_t);
+//   diagonal part, per 32-step tile j <= w of earlier steps s: the chunk's
+//     scores B_s . C_t (a 32 x 32 tile with s as rows, from 3a, the next tile's
+//     load issued before the current one is used), masked (s <= t) and scaled
+//     by exp(ell_t - ell_s) Delta_s, taken off the diagonal as
+//     exp(ell_t - ell_ref) exp(ell_ref - ell_s) Delta_s with ell_ref the value
+//     at the end of tile j (both factors at most 1; the second kept per step in
+//     LDS) and formed directly on the diagonal tile, turned into the A operand
+//     (t as rows, s as k) by exchanging register halves across the half-waves,
+//     times X (K = s, transposing LDS reads);
 //   then + D x and one bf16 store per element.
-__global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(
+// The waves' work grows with w (1 to 8 score tiles); two workgroups per compute
+// unit keep its SIMDs busy meanwhile.
+constexpr int kScanThreads = 2 * kQ;
+
+__global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ dt, const float* __restrict__ A,
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ C, const float* __restrict__ D,
-    const float* __restrict__ dt_bias, const uint16_t* __restrict__ Sin_hi,
-    const uint16_t* __restrict__ Sin_lo, const float* __restrict__ scores, uint16_t* __restrict__ y,
+    const float* __restrict__ dt_bias, const float* __restrict__ Sin, const float* __restrict__ scores,
+    uint16_t* __restrict__ y,
     SsdDims g) {
-  __shared__ float s_delta[kQ], s_ell[kQ], s_wave[4], s_v[kQ];
-  __shared__ __align__(16) uint16_t s_x[kP][kQ + kPad];  // X^T of the chunk
+  constexpr int ldx = kP + kPad, ldsn = kN + kPad;
+  __shared__ float s_delta[kQ], s_ell[kQ], s_wave[kScanThreads / 64], s_v[kQ];
+  __shared__ __align__(16) uint16_t s_x[kQ][ldx];    // X of the chunk, [s][p]
+  // S_in as a bf16 pair, [hi / lo][p][n]; once every wave has used it, the
+  // space holds each wave's 32 x 64 output tile (bf16, [t][p])
+  __shared__ __align__(16) uint16_t s_st[2][kP][ldsn];
+  auto& s_sh = s_st[0];
+  auto& s_sl = s_st[1];
+  static_assert(kScanThreads / 64 * 32 * kP <= 2 * kP * ldsn, "output tiles fit the state space");
   const int c = blockIdx.x;
   const int64_t h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lo = lane & 31, hi = lane >> 5;
   const int64_t grp = h / (g.nheads / g.ngroups);
   const int64_t t_base = static_cast<int64_t>(c) * kQ;
+  // staging loads first, in 16-byte pieces: X (eight per step; rows past the
+  // sequence's end load the last row, no branch, and are zeroed) and S_in
+  constexpr int kXPieces = kQ * kP / 8 / kScanThreads, kSPieces = kP * kN / 4 / kScanThreads;
+  u16x8 xv[kXPieces];
+  f32x4 sv[kSPieces];
+#pragma unroll
+  for (int k = 0; k < kXPieces; ++k) {
+    const int id = tid + kScanThreads * k;
+    const int64_t t = t_base + (id >> 3);
+    const int64_t tr = t < g.seqlen ? t : g.seqlen - 1;
+    xv[k] = *reinterpret_cast<const u16x8*>(x + ((b * g.seqlen + tr) * g.nheads + h) * kP + 8 * (id & 7));
+    if (t >= g.seqlen) xv[k] = u16x8{};
+  }
+  const int64_t sin_off = (((b * g.nheads + h) * g.chunks + c) * kP) * kN;
+#pragma unroll
+  for (int k = 0; k < kSPieces; ++k)
+    sv[k] = *reinterpret_cast<const f32x4*>(Sin + sin_off + (tid + kScanThreads * k) * 4);
   chunk_decay(dt, dt_bias ? dt_bias[h] : 0.0f, A[h], g, b, h, c, s_delta, s_ell, s_wave);
   // per step s: exp(ell_ref - ell_s) Delta_s, ell_ref at the end of the step's 32-step tile
-  s_v[tid] = hw_exp2((s_ell[tid | 31] - s_ell[tid]) * kLog2e) * s_delta[tid];
-  // X^T of the chunk into LDS: thread -> step tid, all 64 channels (16-byte loads)
-  {
-    const int64_t t = t_base + tid;
-    const u16x8* xr = reinterpret_cast<const u16x8*>(x + ((b * g.seqlen + t) * g.nheads + h) * kP);
+  if (tid < kQ) s_v[tid] = hw_exp2((s_ell[tid | 31] - s_ell[tid]) * kLog2e) * s_delta[tid];
 #pragma unroll
-    for (int q = 0; q < kP / 8; ++q) {
-      const u16x8 v = t < g.seqlen ? xr[q] : u16x8{};
+  for (int k = 0; k < kXPieces; ++k) {
+    const int id = tid + kScanThreads * k;
+    *reinterpret_cast<u16x8*>(&s_x[id >> 3][8 * (id & 7)]) = xv[k];
+  }
+  // S_in as a bf16 pair hi + lo (hi + lo = S_in to about 2^-17 relative)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s_x[8 * q + k][tid] = v[k];
+  for (int k = 0; k < kSPieces; ++k) {
+    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+    const int id = tid + kScanThreads * k;
+    u16x4 vh, vl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vh[e] = to_bf16(sv[k][e]);
+      vl[e] = to_bf16(sv[k][e] - from_bf16(vh[e]));
     }
+    *reinterpret_cast<u16x4*>(&s_sh[id >> 5][4 * (id & 31)]) = vh;
+    *reinterpret_cast<u16x4*>(&s_sl[id >> 5][4 * (id & 31)]) = vl;
   }
   __syncthreads();
   const float Dh = D ? D[h] : 0.0f;
-  const int64_t sin_off = (((b * g.nheads + h) * g.chunks + c) * kP) * kN;
-  const uint16_t* sin_hi = Sin_hi + sin_off;
-  const uint16_t* sin_lo = Sin_lo + sin_off;
   const float* tiles = scores + ((b * g.chunks + c) * g.ngroups + grp) * (kTiles * 1024);
 
-  // the 8 bf16 at state offset 8 * hi + 16 kb of row t of B or C (zeros past the end)
-  auto bc_frag = [&](const uint16_t* T, int64_t t, int kb) -> bf16x8 {
-    if (t >= g.seqlen) return bf16x8{};
-    return load8(T + ((b * g.seqlen + t) * g.ngroups + grp) * kN + 16 * kb + 8 * hi);
+  // one 32-step tile of scores (16 values per lane) into registers
+  auto load_tile = [&](f32x4* buf, const float* tp) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) buf[r4] = *reinterpret_cast<const f32x4*>(tp + r4 * 256);
   };
 
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    const int i = which == 0 ? wv : 7 - wv;  // this wave's 32-step tile
+  {
+    const int i = wv;  // this wave's 32-step tile
     const int64_t t_row = t_base + 32 * i + lo;  // the step of this lane's C row
+    // C fragments: the 8 bf16 at state offset 8 * hi + 16 kb of row t (rows past
+    // the end load the last row and are zeroed)
     bf16x8 cf[kN / 16];
+    {
+      const int64_t tr = t_row < g.seqlen ? t_row : g.seqlen - 1;
+      const uint16_t* crow = C + ((b * g.seqlen + tr) * g.ngroups + grp) * kN + 8 * hi;
 #pragma unroll
-    for (int kb = 0; kb < kN / 16; ++kb) cf[kb] = bc_frag(C, t_row, kb);
+      for (int kb = 0; kb < kN / 16; ++kb) cf[kb] = load8(crow + 16 * kb);
+      if (t_row >= g.seqlen) {
+#pragma unroll
+        for (int kb = 0; kb < kN / 16; ++kb) cf[kb] = bf16x8{};
+      }
+    }
+    // score tiles (i, 0..i) are consecutive; the first one's load goes out now
+    const float* trow = tiles + tile_index(i, 0) * 1024 + lane * 4;
+    f32x4 bufA[4], bufB[4];
+    load_tile(bufA, trow);
+    // all of these loads are issued before any of them is used
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 acc[2] = {};
     // inherited state: C_t S_in
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
       for (int kb = 0; kb < kN / 16; ++kb) {
-        const int64_t o = (pt * 32 + lo) * kN + 16 * kb + 8 * hi;
-        acc[pt] = mfma(cf[kb], load8(sin_hi + o), acc[pt]);
-        acc[pt] = mfma(cf[kb], load8(sin_lo + o), acc[pt]);
+        acc[pt] = mfma(cf[kb], load8(&s_sh[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
+        acc[pt] = mfma(cf[kb], load8(&s_sl[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc[pt][r] *= hw_exp2(s_ell[32 * i + 8 * (r >> 2) + 4 * hi + (r & 3)] * kLog2e);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float f = hw_exp2(s_ell[32 * i + 8 * (r >> 2) + 4 * hi + (r & 3)] * kLog2e);
+      acc[0][r] *= f;
+      acc[1][r] *= f;
+    }
+    // every wave is done with S_in: its space takes the output tiles from here on
+    __syncthreads();
     // diagonal blocks
     const int t_loc = 32 * i + lo;          // this lane's column step in the score tile
     const float ell_t = s_ell[t_loc];
-    for (int j = 0; j <= i; ++j) {
-      const float* tp = tiles + tile_index(i, j) * 1024 + lane;
-      float sc[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = tp[r * 64];
-      // mask and scale: element (s, t), s = 32 j + row(r)
-      if (j < i) {
-        // every s precedes every t: both factors are at most 1
-        const float u_t = hw_exp2((ell_t - s_ell[32 * j + 31]) * kLog2e);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sc[r] *= u_t * s_v[32 * j + 8 * (r >> 2) + 4 * hi + (r & 3)];
-      } else {
-        // the diagonal tile: ell_t - ell_ref may be positive, so the weight is
-        // formed directly
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int s_loc = 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const float wgt = hw_exp2((ell_t - s_ell[s_loc]) * kLog2e) * s_delta[s_loc];
-          sc[r] = s_loc <= t_loc ? sc[r] * wgt : 0.0f;
-        }
-      }
+    // masked and scaled tile (s as rows) -> A operand (t as rows, s as k) -> times X
+    auto apply = [&](float* sc, int j) {
       // registers r and r + 4 swapped across the half-waves: lane l then holds
       // the eight consecutive s of k-half (l / 32) for step t = l % 32
       float e[16];
@@ -367,44 +473,88 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_chunk_scan_kernel(
         const bf16x8 aop = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
-          acc[pt] = mfma(aop, load8(&s_x[pt * 32 + lo][32 * j + 16 * q + 8 * hi]), acc[pt]);
+          acc[pt] = mfma(aop, lds_kmajor(&s_x[32 * j + 16 * q][pt * 32], ldx, lane), acc[pt]);
       }
+    };
+    // tile j < i: every s precedes every t, both factors are at most 1
+    auto off_diag = [&](const f32x4* buf, int j) {
+      const float u_t = hw_exp2((ell_t - s_ell[32 * j + 31]) * kLog2e);
+      float sc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sc[r] = buf[r >> 2][r & 3] * (u_t * s_v[32 * j + 8 * (r >> 2) + 4 * hi + (r & 3)]);
+      apply(sc, j);
+    };
+    // tile i: ell_t - ell_ref may be positive, so the weight is formed directly
+    auto diag = [&](const f32x4* buf) {
+      float sc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int s_loc = 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float wgt = hw_exp2(fminf(ell_t - s_ell[s_loc], 0.0f) * kLog2e) * s_delta[s_loc];
+        sc[r] = (s_loc <= t_loc ? buf[r >> 2][r & 3] : 0.0f) * wgt;
+      }
+      apply(sc, i);
+    };
+    // two buffers in turn: the next tile's load is in flight while one is used
+    int j = 0;
+    for (; j + 1 < i; j += 2) {
+      load_tile(bufB, trow + (j + 1) * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+      off_diag(bufA, j);
+      load_tile(bufA, trow + (j + 2) * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+      off_diag(bufB, j + 1);
     }
-    // epilogue: + D x, store (rows past the sequence's end dropped)
+    if (j < i) {
+      load_tile(bufB, trow + i * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+      off_diag(bufA, j);
+      diag(bufB);
+    } else {
+      diag(bufA);
+    }
+    // epilogue: + D x into this wave's output tile in LDS, then 16-byte stores
+    // of whole rows through a buffer resource that ends with the sequence
+    // (rows past its end are dropped)
+    uint16_t* yt = &s_st[0][0][0] + wv * 32 * kP;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int tl = 32 * i + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const int64_t t = t_base + tl;
-        const int p = pt * 32 + lo;
-        if (t < g.seqlen) {
-          const float v = fmaf(Dh, from_bf16(s_x[p][tl]), acc[pt][r]);
-          y[((b * g.seqlen + t) * g.nheads + h) * kP + p] = to_bf16(v);
-        }
+        const int tr = 8 * (r >> 2) + 4 * hi + (r & 3);
+        yt[tr * kP + pt * 32 + lo] = to_bf16(fmaf(Dh, from_bf16(s_x[32 * i + tr][pt * 32 + lo]), acc[pt][r]));
       }
+    }
+    const int64_t t0 = t_base + 32 * i;
+    const int64_t rows = g.seqlen - t0 < 32 ? g.seqlen - t0 : 32;
+    const int64_t row_bytes = g.nheads * kP * 2;
+    const auto rsrc = make_rsrc(y + ((b * g.seqlen + t0) * g.nheads + h) * kP,
+                                rows > 0 ? static_cast<uint32_t>((rows - 1) * row_bytes + kP * 2) : 0u);
+#pragma unroll
+    for (int k = 0; k < 32 * kP / 8 / 64; ++k) {
+      const int id = lane + 64 * k, row = id >> 3, col = 8 * (id & 7);
+      const u16x8 v = *reinterpret_cast<const u16x8*>(yt + row * kP + col);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc,
+                                             static_cast<uint32_t>(row * row_bytes + col * 2), 0, 0);
     }
   }
 }
 
 }  // namespace
 
-// Workspace: the chunk states (fp32), the chunks' decays (fp32), the states
-// entering the chunks (two bf16 arrays), the chunks' score tiles (fp32), each
-// 256-byte aligned.
+// Workspace: the states entering the chunks (fp32), then the chunks' score
+// tiles (fp32), each 256-byte aligned.
 struct SsdWs {
-  size_t sc, ell, sin_hi, sin_lo, scores, total;
+  size_t sin, scores, total;
 };
 SsdWs ssd_ws_layout(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ngroups) {
   const int64_t chunks = (seqlen + kQ - 1) / kQ;
   const size_t states = static_cast<size_t>(batch * nheads * chunks) * kP * kN;
   auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
   SsdWs w;
-  w.sc = 0;
-  w.ell = r256(states * sizeof(float));
-  w.sin_hi = w.ell + r256(static_cast<size_t>(batch * nheads * chunks) * sizeof(float));
-  w.sin_lo = w.sin_hi + r256(states * sizeof(uint16_t));
-  w.scores = w.sin_lo + r256(states * sizeof(uint16_t));
+  w.sin = 0;
+  w.scores = r256(states * sizeof(float));
   w.total = w.scores + r256(static_cast<size_t>(batch * chunks * ngroups) * kTiles * 1024 *
                            sizeof(float));
   return w;
@@ -422,40 +572,32 @@ hipError_t launch_ssd_fwd(const SsdProblem& p, void* workspace, hipStream_t stre
   g.nheads = p.nheads;
   g.ngroups = p.ngroups;
   g.chunks = static_cast<int>((p.seqlen + kQ - 1) / kQ);
-  const int64_t per_head = static_cast<int64_t>(kP) * kN;
-  if (p.seqlen == 0) {
-    if (!p.last_state) return hipSuccess;
-    // no steps: the final state is h0 (or 0); the state pass with no chunks
-    const int64_t n = p.batch * p.nheads * per_head;
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, nullptr, nullptr, p.h0, nullptr, nullptr,
-                       p.last_state, g);
-    return hipGetLastError();
-  }
-  const SsdWs wl = ssd_ws_layout(p.batch, p.seqlen, p.nheads, p.ngroups);
-  char* ws = static_cast<char*>(workspace);
-  float* Sc = reinterpret_cast<float*>(ws + wl.sc);
-  float* ell = reinterpret_cast<float*>(ws + wl.ell);
-  uint16_t* Sin_hi = reinterpret_cast<uint16_t*>(ws + wl.sin_hi);
-  uint16_t* Sin_lo = reinterpret_cast<uint16_t*>(ws + wl.sin_lo);
-  float* scores = reinterpret_cast<float*>(ws + wl.scores);
   const auto* x = static_cast<const uint16_t*>(p.x);
   const auto* dt = static_cast<const uint16_t*>(p.dt);
   const auto* B = static_cast<const uint16_t*>(p.B);
   const auto* C = static_cast<const uint16_t*>(p.C);
-  const dim3 grid(static_cast<unsigned>(g.chunks), static_cast<unsigned>(p.nheads),
-                  static_cast<unsigned>(p.batch));
-  hipLaunchKernelGGL(ssd_chunk_state_kernel, grid, dim3(kThreads), 0, stream, x, dt, p.A, B,
-                     p.dt_bias, Sc, ell, g);
-  const int64_t n = p.batch * p.nheads * per_head;
-  hipLaunchKernelGGL(ssd_state_pass_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, Sc, ell, p.h0, Sin_hi, Sin_lo, p.last_state, g);
+  const dim3 heads(static_cast<unsigned>(p.nheads), static_cast<unsigned>(p.batch));
+  if (p.seqlen == 0) {
+    // no steps: the final state is h0 (or 0)
+    if (!p.last_state) return hipSuccess;
+    hipLaunchKernelGGL(ssd_chunk_state_kernel, heads, dim3(kThreads), 0, stream, x, dt, p.A, B,
+                       p.dt_bias, p.h0, nullptr, p.last_state, g);
+    return hipGetLastError();
+  }
+  const SsdWs wl = ssd_ws_layout(p.batch, p.seqlen, p.nheads, p.ngroups);
+  char* ws = static_cast<char*>(workspace);
+  float* Sin = reinterpret_cast<float*>(ws + wl.sin);
+  float* scores = reinterpret_cast<float*>(ws + wl.scores);
+  hipLaunchKernelGGL(ssd_chunk_state_kernel, heads, dim3(kThreads), 0, stream, x, dt, p.A, B,
+                     p.dt_bias, p.h0, Sin, p.last_state, g);
   hipLaunchKernelGGL(ssd_chunk_scores_kernel,
-                     dim3(static_cast<unsigned>(g.chunks), static_cast<unsigned>(p.ngroups),
+                     dim3(static_cast<unsigned>(g.chunks * kScoreBlocks), static_cast<unsigned>(p.ngroups),
                           static_cast<unsigned>(p.batch)),
                      dim3(kThreads), 0, stream, B, C, scores, g);
-  hipLaunchKernelGGL(ssd_chunk_scan_kernel, grid, dim3(kThreads), 0, stream, x, dt, p.A, B, C, p.D,
-                     p.dt_bias, Sin_hi, Sin_lo, scores, static_cast<uint16_t*>(p.out), g);
+  const dim3 grid(static_cast<unsigned>(g.chunks), static_cast<unsigned>(p.nheads),
+                  static_cast<unsigned>(p.batch));
+  hipLaunchKernelGGL(ssd_chunk_scan_kernel, grid, dim3(kScanThreads), 0, stream, x, dt, p.A, B, C, p.D,
+                     p.dt_bias, Sin, scores, static_cast<uint16_t*>(p.out), g);
   return hipGetLastError();
 }
 
