@@ -33,7 +33,8 @@ namespace {
 constexpr int kQ = 256;       // chunk length (steps)
 constexpr int kP = 64;        // head dimension
 constexpr int kN = 128;       // state size
-constexpr int kThreads = 256; // four waves
+constexpr int kThreads = 256; // four waves, one step of a chunk per thread
+static_assert(kThreads == kQ, "the chunk-state kernel scans one step per thread");
 constexpr int kSBlk = 64;     // steps per LDS block of the chunk-state product
 constexpr int kPad = 8;       // bf16 padding of LDS rows (keeps rows 16-byte aligned, spreads banks)
 constexpr int kWidePad = 32;  // padding that puts the four rows of a transposing read on distinct banks
