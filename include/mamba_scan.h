@@ -183,6 +183,63 @@ mamba_status mamba_state_update(const mamba_scan_desc *desc, float *state,
                                 const float *delta_bias, void *out,
                                 void *stream);
 
+/*
+ * Strided token tensors. A caller whose x, delta, z, out, B or C are column
+ * slices of wider row-major tensors (x and z as the two halves of an input
+ * projection's output rows, B and C as slices of another projection's rows:
+ * "Mamba and selective state spaces, from first principles", section "The
+ * Mamba block", and section "Selection" for B_t, C_t computed per token from
+ * x_t) passes the row strides instead of copying. A row is one time step of
+ * one batch row for mamba_scan_fwd_strided (batch row b's first row is row
+ * b * seqlen, so that batch row b starts b * seqlen * stride elements in) and
+ * one batch row for mamba_state_update_strided. Strides count elements of
+ * the io dtype; 0 means contiguous rows (dim for x, delta, z, out;
+ * G * dstate for B and C). Elements within a row stay contiguous; B and C
+ * share one stride. A stride below its row length returns
+ * MAMBA_ERR_INVALID_ARG, one above 2^26 MAMBA_ERR_UNSUPPORTED. Overlap checks
+ * use each tensor's span (first to last element): out may not interleave
+ * with an input's rows. Inputs may share memory (x and z interleaved in one
+ * buffer are fine). The direct global-to-LDS copy path is used when every
+ * row of x, delta, z and out starts 16- (or 4-) byte aligned; otherwise the
+ * register-staged path is taken, with the same results.
+ */
+typedef struct mamba_scan_strides {
+  int64_t x, delta, z, out; /* elements between consecutive rows, or 0 */
+  int64_t bc;               /* B and C, or 0                          */
+} mamba_scan_strides;
+
+/* Workspace of mamba_scan_fwd_strided (the segment plan keeps every in-segment
+ * byte offset within 31 bits, so the widest stride can change it). strides
+ * may be NULL (then it equals mamba_scan_workspace_size). 0 for an invalid
+ * descriptor or stride. */
+size_t mamba_scan_workspace_size_strided(const mamba_scan_desc *desc,
+                                         const mamba_scan_strides *strides);
+
+/* mamba_scan_fwd_init with strided token tensors (strides may be NULL: all
+ * contiguous). Same semantics, conventions and results as mamba_scan_fwd_init;
+ * workspace sized by mamba_scan_workspace_size_strided. */
+mamba_status mamba_scan_fwd_strided(const mamba_scan_desc *desc,
+                                    const mamba_scan_strides *strides,
+                                    const void *x, const void *delta,
+                                    const float *A, const void *B, const void *C,
+                                    const float *D, const void *z,
+                                    const float *delta_bias, const float *h0,
+                                    void *out, float *last_state,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* mamba_state_update with strided token tensors (strides may be NULL): row b
+ * of x, delta, z, out starts b * stride elements in; B and C likewise with
+ * stride bc. The state stays contiguous (batch, dim, dstate). */
+mamba_status mamba_state_update_strided(const mamba_scan_desc *desc,
+                                        const mamba_scan_strides *strides,
+                                        float *state, const void *x,
+                                        const void *delta, const float *A,
+                                        const void *B, const void *C,
+                                        const float *D, const void *z,
+                                        const float *delta_bias, void *out,
+                                        void *stream);
+
 /* Static name of a status code ("MAMBA_OK", ...). */
 const char *mamba_status_string(int status);
 

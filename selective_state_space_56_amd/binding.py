@@ -40,6 +40,12 @@ def _groups(B, time_axis=True):
     return B.shape[-2] if B.dim() == (4 if time_axis else 3) else 1
 
 
+class Strides(ctypes.Structure):
+    """mamba_scan_strides: elements between consecutive rows (0 = contiguous)."""
+    _fields_ = [("x", ctypes.c_int64), ("delta", ctypes.c_int64), ("z", ctypes.c_int64),
+                ("out", ctypes.c_int64), ("bc", ctypes.c_int64)]
+
+
 class SsdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
@@ -86,6 +92,15 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_state_update.restype = ctypes.c_int
         lib.mamba_state_update.argtypes = [ctypes.POINTER(Desc), fp, vp, vp, fp, vp, vp, fp, vp, fp,
                                            vp, vp]
+        sp = ctypes.POINTER(Strides)
+        lib.mamba_scan_workspace_size_strided.restype = sz
+        lib.mamba_scan_workspace_size_strided.argtypes = [ctypes.POINTER(Desc), sp]
+        lib.mamba_scan_fwd_strided.restype = ctypes.c_int
+        lib.mamba_scan_fwd_strided.argtypes = [ctypes.POINTER(Desc), sp, vp, vp, fp, vp, vp, fp, vp,
+                                               fp, fp, vp, fp, vp, sz, vp]
+        lib.mamba_state_update_strided.restype = ctypes.c_int
+        lib.mamba_state_update_strided.argtypes = [ctypes.POINTER(Desc), sp, fp, vp, vp, fp, vp, vp,
+                                                   fp, vp, fp, vp, vp]
         lib.mamba_conv1d_fwd.restype = ctypes.c_int
         lib.mamba_conv1d_fwd.argtypes = [ctypes.POINTER(ConvDesc), vp, fp, fp, vp, vp, vp, vp]
         lib.mamba_conv1d_update.restype = ctypes.c_int
@@ -128,6 +143,48 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _row_stride(t, name, shape, dtype, device, rows_axis):
+    """Checks a token tensor that may be a column slice of a wider row-major
+    tensor: device, dtype, shape; the dimensions after `rows_axis` packed
+    (one row of contiguous elements); the dimensions up to `rows_axis` one run
+    of equally spaced rows. Returns the row stride in elements, or None for
+    None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    inner = 1
+    for ax in range(t.dim() - 1, rows_axis, -1):
+        inner *= t.shape[ax]
+    if t.numel() == 0:   # no elements: the strides of an empty tensor carry no layout
+        return inner
+    inner = 1
+    for ax in range(t.dim() - 1, rows_axis, -1):
+        if t.shape[ax] > 1 and t.stride(ax) != inner:
+            raise ValueError(f"{name}: elements within a row must be contiguous")
+        inner *= t.shape[ax]
+    # the row axes (0 .. rows_axis), flattened, must be one arithmetic run
+    stride, count = None, 1
+    for ax in range(rows_axis, -1, -1):
+        if t.shape[ax] == 1:
+            continue
+        if stride is None:
+            stride, count = t.stride(ax), t.shape[ax]
+            if stride == 0:
+                raise ValueError(f"{name}: broadcast (zero-stride) rows are not supported")
+        else:
+            if t.stride(ax) != stride * count:
+                raise ValueError(f"{name}: rows must be equally spaced (batch rows one after another)")
+            count *= t.shape[ax]
+    return inner if stride is None else stride
+
+
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -154,6 +211,9 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     (batch, dim, N) float32 (None if not requested). ``segments`` > 0 forces
     the number of time segments; ``zoh`` selects the exact zero-order-hold
     input weight (MAMBA_SCAN_ZOH) instead of the first-order Delta B.
+    x, delta, z, B, C and out may be column slices of wider tensors (rows of
+    contiguous elements, equally spaced): then the call goes to
+    mamba_scan_fwd_strided with their row strides.
     """
     lib = load_library()
     if x.dim() != 3 or A.dim() != 2:
@@ -166,24 +226,38 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     io = x.dtype
     if io not in _IO:
         raise TypeError(f"unsupported io dtype {io}")
-    _need(delta, "delta", (batch, L, dim), io, dev)
-    _need(z, "z", (batch, L, dim), io, dev)
+    # token tensors may be column slices of wider row-major tensors (one row
+    # per step): then the strided entry point takes their row strides
+    sx = _row_stride(x, "x", (batch, L, dim), io, dev, 1)
+    sd = _row_stride(delta, "delta", (batch, L, dim), io, dev, 1)
+    sz = _row_stride(z, "z", (batch, L, dim), io, dev, 1)
     G = _groups(B)
     bshape = (batch, L, G, N) if B.dim() == 4 else (batch, L, N)
-    _need(B, "B", bshape, io, dev)
-    _need(C, "C", bshape, io, dev)
+    sb = _row_stride(B, "B", bshape, io, dev, 1)
+    sc = _row_stride(C, "C", bshape, io, dev, 1)
+    if sb != sc:
+        raise ValueError("B and C must have the same row stride")
     _need(A, "A", (dim, N), torch.float32, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
-    _need(x, "x", (batch, L, dim), io, dev)
     _need(h0, "h0", (batch, dim, N), torch.float32, dev)
     if out is None:
         out = torch.empty((batch, L, dim), dtype=io, device=dev)
-    _need(out, "out", (batch, L, dim), io, dev)
+    so = _row_stride(out, "out", (batch, L, dim), io, dev, 1)
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
     d = Desc(batch, L, dim, N, _IO[io], int(segments) | (ZOH_FLAG if zoh else 0), G)
+    strides = Strides(sx, sd, sz or 0, so, sb)
+    if (sx, sd, sz or dim, so, sb) != (dim, dim, dim, dim, G * N):
+        ws_bytes = int(lib.mamba_scan_workspace_size_strided(ctypes.byref(d), ctypes.byref(strides)))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        st = lib.mamba_scan_fwd_strided(ctypes.byref(d), ctypes.byref(strides), _ptr(x), _ptr(delta),
+                                        _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                        _ptr(h0), _ptr(out), _ptr(last_state), _ptr(ws),
+                                        ctypes.c_size_t(ws_bytes), _stream(dev))
+        _check(lib, st)
+        return out, last_state
     ws_bytes = int(lib.mamba_scan_workspace_size(ctypes.byref(d)))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     if h0 is None:
@@ -266,7 +340,8 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
                  zoh=False):
     """One decode token: advances ``state`` (batch, dim, N) float32 in place and
     returns out (batch, dim). x, delta, z: (batch, dim); B, C: (batch, N).
-    ``zoh`` selects the exact zero-order-hold input weight."""
+    ``zoh`` selects the exact zero-order-hold input weight. Token tensors may
+    be column slices of wider tensors (mamba_state_update_strided)."""
     lib = load_library()
     if x.dim() != 2 or A.dim() != 2:
         raise ValueError("x must be (batch, dim) and A (dim, N)")
@@ -279,22 +354,31 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, o
     if io not in _IO:
         raise TypeError(f"unsupported io dtype {io}")
     _need(state, "state", (batch, dim, N), torch.float32, dev)
-    _need(delta, "delta", (batch, dim), io, dev)
-    _need(z, "z", (batch, dim), io, dev)
+    sx = _row_stride(x, "x", (batch, dim), io, dev, 0)
+    sd = _row_stride(delta, "delta", (batch, dim), io, dev, 0)
+    sz = _row_stride(z, "z", (batch, dim), io, dev, 0)
     G = _groups(B, time_axis=False)
     bshape = (batch, G, N) if B.dim() == 3 else (batch, N)
-    _need(B, "B", bshape, io, dev)
-    _need(C, "C", bshape, io, dev)
+    sb = _row_stride(B, "B", bshape, io, dev, 0)
+    sc = _row_stride(C, "C", bshape, io, dev, 0)
+    if sb != sc:
+        raise ValueError("B and C must have the same row stride")
     _need(A, "A", (dim, N), torch.float32, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     if out is None:
         out = torch.empty((batch, dim), dtype=io, device=dev)
-    _need(out, "out", (batch, dim), io, dev)
+    so = _row_stride(out, "out", (batch, dim), io, dev, 0)
     d = Desc(batch, 1, dim, N, _IO[io], ZOH_FLAG if zoh else 0, G)
-    st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
-                                _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
-                                _stream(dev))
+    if (sx, sd, sz or dim, so, sb) != (dim, dim, dim, dim, G * N):
+        strides = Strides(sx, sd, sz or 0, so, sb)
+        st = lib.mamba_state_update_strided(ctypes.byref(d), ctypes.byref(strides), _ptr(state),
+                                            _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                            _ptr(z), _ptr(delta_bias), _ptr(out), _stream(dev))
+    else:
+        st = lib.mamba_state_update(ctypes.byref(d), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                                    _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(out),
+                                    _stream(dev))
     _check(lib, st)
     return out
 

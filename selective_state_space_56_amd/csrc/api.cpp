@@ -97,6 +97,49 @@ mamba_status check_groups(const mamba_scan_desc* d, const char* who, bool tiles)
   return MAMBA_OK;
 }
 
+// Row strides of the token tensors, resolved: 0 in the caller's struct (or no
+// struct) means contiguous rows.
+struct Rows {
+  int64_t x, d, z, o, bc;
+};
+
+mamba_status resolve_rows(const mamba_scan_strides* s, const mamba_scan_desc* d, const char* who,
+                          Rows& r) {
+  const int64_t G = groups_of(d);
+  const int64_t bc_min = G * d->dstate;
+  r = Rows{d->dim, d->dim, d->dim, d->dim, bc_min};
+  if (!s) return MAMBA_OK;
+  const struct {
+    const char* name;
+    int64_t given, min;
+    int64_t* dst;
+  } f[] = {{"x", s->x, d->dim, &r.x}, {"delta", s->delta, d->dim, &r.d}, {"z", s->z, d->dim, &r.z},
+           {"out", s->out, d->dim, &r.o}, {"bc", s->bc, bc_min, &r.bc}};
+  for (const auto& e : f) {
+    if (e.given == 0) continue;
+    if (e.given < e.min)
+      return fail(MAMBA_ERR_INVALID_ARG, "%s: %s stride %lld is below its row length %lld", who,
+                  e.name, (long long)e.given, (long long)e.min);
+    // one row of one tensor (stride * 4 bytes) must stay far below 2^31
+    if (e.given > (int64_t(1) << 26))
+      return fail(MAMBA_ERR_UNSUPPORTED, "%s: %s stride %lld too large", who, e.name,
+                  (long long)e.given);
+    *e.dst = e.given;
+  }
+  return MAMBA_OK;
+}
+
+int64_t widest(const Rows& r) {
+  int64_t w = r.x;
+  for (int64_t v : {r.d, r.z, r.o, r.bc}) w = v > w ? v : w;
+  return w;
+}
+
+// Bytes spanned by `rows` rows of `len` elements `stride` elements apart.
+size_t span_bytes(int64_t rows, int64_t stride, int64_t len, size_t eb) {
+  return rows > 0 ? static_cast<size_t>((rows - 1) * stride + len) * eb : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,23 +156,31 @@ const char* mamba_status_string(int s) {
 
 const char* mamba_last_error(void) { return g_last_error.c_str(); }
 
-size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
-  if (check_desc(d, "mamba_scan_workspace_size") != MAMBA_OK) return 0;
+size_t mamba_scan_workspace_size_strided(const mamba_scan_desc* d, const mamba_scan_strides* s) {
+  const char* who = "mamba_scan_workspace_size";
+  if (check_desc(d, who) != MAMBA_OK) return 0;
   if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH)) return 0;
-  if (check_groups(d, "mamba_scan_workspace_size", true) != MAMBA_OK) return 0;
+  if (check_groups(d, who, true) != MAMBA_OK) return 0;
+  Rows r;
+  if (resolve_rows(s, d, who, r) != MAMBA_OK) return 0;
   return mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
-                          forced_segments(d))
+                          forced_segments(d), widest(r))
       .workspace_bytes;
+}
+
+size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
+  return mamba_scan_workspace_size_strided(d, nullptr);
 }
 
 }  // extern "C"
 
 namespace {
 
-mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void* x,
-                           const void* delta, const float* A, const void* B, const void* C,
-                           const float* D, const void* z, const float* delta_bias, const float* h0,
-                           void* out, float* last_state, void* workspace, size_t workspace_bytes,
+mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
+                           const mamba_scan_strides* strides, const void* x, const void* delta,
+                           const float* A, const void* B, const void* C, const float* D,
+                           const void* z, const float* delta_bias, const float* h0, void* out,
+                           float* last_state, void* workspace, size_t workspace_bytes,
                            void* stream) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
@@ -137,6 +188,11 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
     return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who,
                 d->flags & ~(0xffffu | MAMBA_SCAN_ZOH));
   if ((st = check_groups(d, who, true)) != MAMBA_OK) return st;
+  Rows rs;
+  if ((st = resolve_rows(strides, d, who, rs)) != MAMBA_OK) return st;
+  // every element offset of a strided tensor stays within 2^40 elements
+  if (d->batch * d->seqlen > 0 && widest(rs) > (int64_t(1) << 40) / (d->batch * d->seqlen))
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: problem too large", who);
   const int64_t G = groups_of(d);
   const int64_t rows = d->batch * d->dim;
   const int64_t tokens = d->batch * d->seqlen;
@@ -149,8 +205,8 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
     if (!C) return fail(MAMBA_ERR_INVALID_ARG, "%s: C is NULL", who);
     if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
   }
-  const mscan::ScanPlan plan =
-      mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate), forced_segments(d));
+  const mscan::ScanPlan plan = mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
+                                                forced_segments(d), widest(rs));
   if (elems > 0 && plan.workspace_bytes > 0) {
     if (!workspace)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who,
@@ -163,17 +219,18 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   }
   const size_t eb = io_bytes(d->io_dtype);
   const size_t N = static_cast<size_t>(d->dstate);
+  const int64_t rowsteps = elems > 0 ? tokens : 0;  // rows of each token tensor
   const Span in[] = {
-      {"x", x, static_cast<size_t>(elems) * eb},
-      {"delta", delta, static_cast<size_t>(elems) * eb},
-      {"z", z, static_cast<size_t>(elems) * eb},
-      {"B", B, static_cast<size_t>(tokens * G) * N * eb},
-      {"C", C, static_cast<size_t>(tokens * G) * N * eb},
+      {"x", x, span_bytes(rowsteps, rs.x, d->dim, eb)},
+      {"delta", delta, span_bytes(rowsteps, rs.d, d->dim, eb)},
+      {"z", z, span_bytes(rowsteps, rs.z, d->dim, eb)},
+      {"B", B, span_bytes(tokens, rs.bc, G * d->dstate, eb)},
+      {"C", C, span_bytes(tokens, rs.bc, G * d->dstate, eb)},
       {"A", A, static_cast<size_t>(d->dim) * N * 4},
       {"D", D, static_cast<size_t>(d->dim) * 4},
       {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
   };
-  const Span o_out{"out", out, static_cast<size_t>(elems) * eb};
+  const Span o_out{"out", out, span_bytes(rowsteps, rs.o, d->dim, eb)};
   const Span o_last{"last_state", last_state, static_cast<size_t>(rows) * N * 4};
   const Span o_ws{"workspace", elems > 0 ? workspace : nullptr, plan.workspace_bytes};
   for (const Span& s : in) {
@@ -197,6 +254,9 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   for (const Span& s : {in[3], in[4]})
     if (s.p && reinterpret_cast<uintptr_t>(s.p) % bc_align)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", who, s.name, bc_align);
+  if ((static_cast<size_t>(rs.bc) * eb) % bc_align)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: B/C rows (stride %lld) are not %zu-byte aligned", who,
+                (long long)rs.bc, bc_align);
   for (const void* p : {static_cast<const void*>(A), static_cast<const void*>(D),
                         static_cast<const void*>(delta_bias), static_cast<const void*>(last_state),
                         static_cast<const void*>(h0)})
@@ -224,6 +284,11 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d, const void
   p.io = d->io_dtype;
   p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
   p.ngroups = G;
+  p.sx = rs.x;
+  p.sd = rs.d;
+  p.sz = rs.z;
+  p.so = rs.o;
+  p.sbc = rs.bc;
   const hipError_t e = mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -238,8 +303,8 @@ mamba_status mamba_scan_fwd(const mamba_scan_desc* d, const void* x, const void*
                             const float* A, const void* B, const void* C, const float* D,
                             const void* z, const float* delta_bias, void* out, float* last_state,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  return scan_fwd_impl("mamba_scan_fwd", d, x, delta, A, B, C, D, z, delta_bias, nullptr, out,
-                       last_state, workspace, workspace_bytes, stream);
+  return scan_fwd_impl("mamba_scan_fwd", d, nullptr, x, delta, A, B, C, D, z, delta_bias, nullptr,
+                       out, last_state, workspace, workspace_bytes, stream);
 }
 
 mamba_status mamba_scan_fwd_init(const mamba_scan_desc* d, const void* x, const void* delta,
@@ -247,15 +312,29 @@ mamba_status mamba_scan_fwd_init(const mamba_scan_desc* d, const void* x, const 
                                  const void* z, const float* delta_bias, const float* h0,
                                  void* out, float* last_state, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  return scan_fwd_impl("mamba_scan_fwd_init", d, x, delta, A, B, C, D, z, delta_bias, h0, out,
-                       last_state, workspace, workspace_bytes, stream);
+  return scan_fwd_impl("mamba_scan_fwd_init", d, nullptr, x, delta, A, B, C, D, z, delta_bias, h0,
+                       out, last_state, workspace, workspace_bytes, stream);
 }
 
-mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const void* x,
-                                const void* delta, const float* A, const void* B, const void* C,
-                                const float* D, const void* z, const float* delta_bias, void* out,
-                                void* stream) {
-  const char* who = "mamba_state_update";
+mamba_status mamba_scan_fwd_strided(const mamba_scan_desc* d, const mamba_scan_strides* strides,
+                                    const void* x, const void* delta, const float* A, const void* B,
+                                    const void* C, const float* D, const void* z,
+                                    const float* delta_bias, const float* h0, void* out,
+                                    float* last_state, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return scan_fwd_impl("mamba_scan_fwd_strided", d, strides, x, delta, A, B, C, D, z, delta_bias, h0,
+                       out, last_state, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+mamba_status state_update_impl(const char* who, const mamba_scan_desc* d,
+                               const mamba_scan_strides* strides, float* state, const void* x,
+                               const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, void* out,
+                               void* stream) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
   if (d->flags & ~MAMBA_SCAN_ZOH)
@@ -266,6 +345,8 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
     return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
   if ((d->batch + 15) / 16 > 65535)
     return fail(MAMBA_ERR_UNSUPPORTED, "%s: batch %lld too large", who, (long long)d->batch);
+  Rows rs;
+  if ((st = resolve_rows(strides, d, who, rs)) != MAMBA_OK) return st;
   const int64_t rows = d->batch * d->dim;
   if (rows == 0) return ok();
   if (!state) return fail(MAMBA_ERR_INVALID_ARG, "%s: state is NULL", who);
@@ -278,17 +359,17 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   const size_t eb = io_bytes(d->io_dtype);
   const size_t N = static_cast<size_t>(d->dstate);
   const Span in[] = {
-      {"x", x, static_cast<size_t>(rows) * eb},
-      {"delta", delta, static_cast<size_t>(rows) * eb},
-      {"z", z, static_cast<size_t>(rows) * eb},
-      {"B", B, static_cast<size_t>(d->batch * G) * N * eb},
-      {"C", C, static_cast<size_t>(d->batch * G) * N * eb},
+      {"x", x, span_bytes(d->batch, rs.x, d->dim, eb)},
+      {"delta", delta, span_bytes(d->batch, rs.d, d->dim, eb)},
+      {"z", z, span_bytes(d->batch, rs.z, d->dim, eb)},
+      {"B", B, span_bytes(d->batch, rs.bc, G * d->dstate, eb)},
+      {"C", C, span_bytes(d->batch, rs.bc, G * d->dstate, eb)},
       {"A", A, static_cast<size_t>(d->dim) * N * 4},
       {"D", D, static_cast<size_t>(d->dim) * 4},
       {"delta_bias", delta_bias, static_cast<size_t>(d->dim) * 4},
   };
   const Span o_state{"state", state, static_cast<size_t>(rows) * N * 4};
-  const Span o_out{"out", out, static_cast<size_t>(rows) * eb};
+  const Span o_out{"out", out, span_bytes(d->batch, rs.o, d->dim, eb)};
   for (const Span& s : in) {
     if (overlaps(o_state, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: state overlaps %s", who, s.name);
     if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
@@ -322,10 +403,36 @@ mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const vo
   p.io = d->io_dtype;
   p.zoh = (d->flags & MAMBA_SCAN_ZOH) != 0;
   p.ngroups = G;
+  p.sx = rs.x;
+  p.sd = rs.d;
+  p.sz = rs.z;
+  p.so = rs.o;
+  p.sbc = rs.bc;
   const hipError_t e = mscan::launch_state_update(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mamba_status mamba_state_update(const mamba_scan_desc* d, float* state, const void* x,
+                                const void* delta, const float* A, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, void* out,
+                                void* stream) {
+  return state_update_impl("mamba_state_update", d, nullptr, state, x, delta, A, B, C, D, z,
+                           delta_bias, out, stream);
+}
+
+mamba_status mamba_state_update_strided(const mamba_scan_desc* d, const mamba_scan_strides* strides,
+                                        float* state, const void* x, const void* delta,
+                                        const float* A, const void* B, const void* C,
+                                        const float* D, const void* z, const float* delta_bias,
+                                        void* out, void* stream) {
+  return state_update_impl("mamba_state_update_strided", d, strides, state, x, delta, A, B, C, D, z,
+                           delta_bias, out, stream);
 }
 
 

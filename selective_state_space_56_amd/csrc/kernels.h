@@ -26,6 +26,10 @@ struct ScanProblem {
   int io;
   bool zoh;            // exact zero-order-hold input weight instead of Delta
   int64_t ngroups;     // G >= 1: B, C are (batch, seqlen, G, dstate); dim / G a multiple of 256
+  // elements between consecutive steps (rows), per tensor: x, Delta_raw, z,
+  // out (at least dim) and B, C (at least G * dstate); batch row b starts at
+  // b * seqlen * stride
+  int64_t sx, sd, sz, so, sbc;
 };
 
 // Time segmentation of a full-sequence scan: the sequence is cut into
@@ -38,7 +42,9 @@ struct ScanPlan {
 };
 
 // forced_segments > 0 overrides the library's choice of time segments.
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments);
+// row_elems: the widest step stride (elements) of the scan's tensors (dim when contiguous)
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments,
+                   int64_t row_elems);
 
 hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* workspace,
                            hipStream_t stream);
@@ -115,6 +121,9 @@ struct DecodeProblem {
   int io;
   bool zoh;            // exact zero-order-hold input weight instead of Delta
   int64_t ngroups;     // G >= 1 dividing dim: B, C are (batch, G, dstate)
+  // elements between consecutive batch rows, per tensor: x, Delta_raw, z, out
+  // (at least dim) and B, C (at least G * dstate)
+  int64_t sx, sd, sz, so, sbc;
 };
 
 hipError_t launch_state_update(const DecodeProblem& p, hipStream_t stream);

@@ -1005,7 +1005,7 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate
     if (v > seqlen / 48) v = seqlen / 48;
     segs = static_cast<int>(v < 1 ? 1 : (v > 4096 ? 4096 : v));
   }
-  plan.seg = plan_scan(batch, seqlen, dim, dstate, segs > 0 ? segs : 1);
+  plan.seg = plan_scan(batch, seqlen, dim, dstate, segs > 0 ? segs : 1, dim);
   if (rows <= 0 || seqlen <= 0) return plan;
   const size_t S = static_cast<size_t>(plan.seg.segments);
   const size_t N = static_cast<size_t>(dstate);

@@ -42,6 +42,8 @@ struct Dims {
   const float* h0;       // state before the first step, (batch, dim, N), or null (zeros)
   int64_t ngroups;       // B and C groups: (batch, seqlen, ngroups, N)
   int64_t group_dim;     // channels per group (a multiple of kBlock when ngroups > 1)
+  // elements between consecutive steps: x, Delta_raw, z, out, and B / C
+  int64_t sx, sd, sz, so, sbc;
 };
 
 enum Mode { kOutput = 0, kAggregate = 1 };
@@ -263,26 +265,31 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     for (int n = 0; n < N; ++n) h[n] = 0.0f;
   }
 
-  // buffer resources at (b, t_begin, first channel of the tile)
-  const int64_t row0 = (b * g.seqlen + t_begin) * g.dim + d0;
-  const uint32_t row_bytes = static_cast<uint32_t>(g.dim * eb);
+  // buffer resources at (b, t_begin, first channel of the tile), per tensor
+  // (each has its own step stride)
+  const int64_t step0 = b * g.seqlen + t_begin;
+  const uint32_t rbx = static_cast<uint32_t>(g.sx * eb), rbd = static_cast<uint32_t>(g.sd * eb);
+  const uint32_t rbz = static_cast<uint32_t>(g.sz * eb), rbo = static_cast<uint32_t>(g.so * eb);
   const int64_t left = g.dim - d0;
   const uint32_t valid_bytes = static_cast<uint32_t>((left < kBlock ? left : kBlock) * eb);
   const uint32_t ch_off = active ? tid * eb : kOffNone;  // this lane's channel in a row
-  // per-lane offset of the tile pieces this lane copies (CW > 0)
-  const uint32_t lane_off = CW != 0 ? tile_lane_offset<IO, (CW != 0 ? CW : 4)>(row_bytes, valid_bytes)
-                                    : 0u;
+  // per-lane offset of the tile pieces this lane copies (CW > 0), per tensor
+  constexpr int kCW = CW != 0 ? CW : 4;
+  const uint32_t lo_x = CW != 0 ? tile_lane_offset<IO, kCW>(rbx, valid_bytes) : 0u;
+  const uint32_t lo_d = CW != 0 ? tile_lane_offset<IO, kCW>(rbd, valid_bytes) : 0u;
+  const uint32_t lo_z = CW != 0 && kZ ? tile_lane_offset<IO, kCW>(rbz, valid_bytes) : 0u;
+  const uint32_t lo_o = CW != 0 ? tile_lane_offset<IO, kCW>(rbo, valid_bytes) : 0u;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, wave-uniform
   // first element of the tile in the segment's first step, per tensor
-  const raw* x0 = x + row0;
-  const raw* dl0 = delta + row0;
-  const raw* z0 = kZ ? z + row0 : x + row0;
-  raw* out0 = out + row0;
+  const raw* x0 = x + step0 * g.sx + d0;
+  const raw* dl0 = delta + step0 * g.sd + d0;
+  const raw* z0 = kZ ? z + step0 * g.sz + d0 : x0;
+  raw* out0 = out + step0 * g.so + d0;
   // the tile's group of B and C (every channel of a tile is in one group)
   const int64_t grp = d0 / g.group_dim;
-  const uint32_t bc_row = static_cast<uint32_t>(g.ngroups * N);  // elements per step
-  const raw* Bp = B + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
-  const raw* Cp = C + ((b * g.seqlen + t_begin) * g.ngroups + grp) * N;
+  const uint32_t bc_row = static_cast<uint32_t>(g.sbc);  // elements per step
+  const raw* Bp = B + step0 * g.sbc + grp * N;
+  const raw* Cp = C + step0 * g.sbc + grp * N;
   // this thread's B/C tile elements: tid, tid + kBlock, ...
   BcOffsets bco[kBcPer];
 #pragma unroll
@@ -293,16 +300,16 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   // in registers on the register-staged path until land() writes them)
   TileRegs<IO> rgx, rgd, rgz;
   auto fetch = [&](int nb, uint32_t t1) {
-    const int64_t at = static_cast<int64_t>(t1) * g.dim;
+    const int64_t at = static_cast<int64_t>(t1);
     const uint32_t left = steps - t1;
     if constexpr (CW != 0) {
-      dma_tile<IO, CW>(x0 + at, left, row_bytes, &st.in[nb][0][0][0], wv, lane_off);
-      dma_tile<IO, CW>(dl0 + at, left, row_bytes, &st.in[nb][1][0][0], wv, lane_off);
-      if (kZ) dma_tile<IO, CW>(z0 + at, left, row_bytes, &st.in[nb][kZi][0][0], wv, lane_off);
+      dma_tile<IO, CW>(x0 + at * g.sx, left, rbx, &st.in[nb][0][0][0], wv, lo_x);
+      dma_tile<IO, CW>(dl0 + at * g.sd, left, rbd, &st.in[nb][1][0][0], wv, lo_d);
+      if (kZ) dma_tile<IO, CW>(z0 + at * g.sz, left, rbz, &st.in[nb][kZi][0][0], wv, lo_z);
     } else {
-      load_tile_regs<IO>(rgx, x0 + at, left, row_bytes, ch_off);
-      load_tile_regs<IO>(rgd, dl0 + at, left, row_bytes, ch_off);
-      if (kZ) load_tile_regs<IO>(rgz, z0 + at, left, row_bytes, ch_off);
+      load_tile_regs<IO>(rgx, x0 + at * g.sx, left, rbx, ch_off);
+      load_tile_regs<IO>(rgd, dl0 + at * g.sd, left, rbd, ch_off);
+      if (kZ) load_tile_regs<IO>(rgz, z0 + at * g.sz, left, rbz, ch_off);
     }
   };
   // this thread's B/C elements of the chunk at step t1, and their LDS stores
@@ -322,8 +329,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   };
   // y tile of the chunk at step t1 from LDS buffer yb to HBM
   auto put_y = [&](int yb, uint32_t t1) {
-    store_tile<IO, CW>(out0 + static_cast<int64_t>(t1) * g.dim, steps - t1, row_bytes,
-                       &st.yo[yb][0][0], lane_off, ch_off);
+    store_tile<IO, CW>(out0 + static_cast<int64_t>(t1) * g.so, steps - t1, rbo,
+                       &st.yo[yb][0][0], lo_o, ch_off);
   };
   auto land = [&](int nb) {
     if constexpr (CW == 0) {
@@ -501,6 +508,11 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.h0 = p.h0;
   g.ngroups = p.ngroups;
   g.group_dim = p.dim / p.ngroups;
+  g.sx = p.sx;
+  g.sd = p.sd;
+  g.sz = p.z ? p.sz : p.sx;
+  g.so = p.so;
+  g.sbc = p.sbc;
   float* ws_h = static_cast<float*>(workspace);
   float* ws_s = ws_h ? ws_h + static_cast<int64_t>(plan.segments - 1) * g.rows * N : nullptr;
   g.tile_flags = ws_s ? reinterpret_cast<uint32_t*>(ws_s + static_cast<int64_t>(plan.segments - 1) *
@@ -583,9 +595,14 @@ hipError_t launch_copy_width(const ScanProblem& p, const ScanPlan& plan, void* w
   constexpr int eb = sizeof(typename IO::raw);
   const auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
   const auto a4 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 4 == 0; };
-  if ((p.dim * eb) % 16 == 0 && a16(p.x) && a16(p.delta) && (!p.z || a16(p.z)))
+  // every row of every tensor must start S-byte aligned (row strides too)
+  const auto rows_ok = [&](int64_t m) {
+    return (p.dim * eb) % m == 0 && (p.sx * eb) % m == 0 && (p.sd * eb) % m == 0 &&
+           (p.so * eb) % m == 0 && (!p.z || (p.sz * eb) % m == 0);
+  };
+  if (rows_ok(16) && a16(p.x) && a16(p.delta) && a16(p.out) && (!p.z || a16(p.z)))
     return launch_typed<N, IO, 16>(p, plan, ws, st);
-  if ((p.dim * eb) % 4 == 0 && a4(p.x) && a4(p.delta) && (!p.z || a4(p.z)))
+  if (rows_ok(4) && a4(p.x) && a4(p.delta) && a4(p.out) && (!p.z || a4(p.z)))
     return launch_typed<N, IO, 4>(p, plan, ws, st);
   return launch_typed<N, IO, 0>(p, plan, ws, st);
 }
@@ -622,7 +639,8 @@ static int device_cus() {
 
 int device_cu_count() { return device_cus(); }
 
-ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments) {
+ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments,
+                   int64_t row_elems) {
   ScanPlan plan{seqlen, 1, 0};
   const int64_t rows = batch * dim;
   if (rows <= 0 || seqlen <= 0) return plan;
@@ -644,8 +662,9 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
   if (segs > 4096) segs = 4096;
   if (segs > seqlen) segs = seqlen;
   if (segs < 1) segs = 1;
-  // every in-segment byte offset (step * dim * 4 at most) must fit in 31 bits
-  const int64_t max_len = ((int64_t(1) << 31) - 1) / (dim * 4) - kChunk;
+  // every in-segment byte offset (step * row stride * 4 at most) must fit in 31 bits
+  const int64_t widest = row_elems > dim ? row_elems : dim;
+  const int64_t max_len = ((int64_t(1) << 31) - 1) / (widest * 4) - kChunk;
   if ((seqlen + segs - 1) / segs > max_len) segs = (seqlen + max_len - 1) / max_len;
   int64_t seg_len = (seqlen + segs - 1) / segs;
   seg_len = (seg_len + kChunk - 1) / kChunk * kChunk;

@@ -42,6 +42,8 @@ struct DecodeKernelArgs {
   int64_t dim;
   int64_t ngroups;    // B and C: (batch, ngroups, N)
   int64_t group_dim;  // channels per group
+  // elements between consecutive batch rows: x, Delta_raw, z, out, and B / C
+  int64_t sx, sd, sz, so, sbc;
 };
 
 // Grid: x = (channel, lane-of-row) pairs, kBlock per workgroup; y = runs of
@@ -82,9 +84,9 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a
     for (int r = 0; r < kGroupRows; ++r) {
       const int64_t b = g0 + r < b1 ? g0 + r : b1 - 1;
       const int64_t row = b * a.dim + d;
-      xf[r] = IO::load(xp + row);
-      draw[r] = IO::load(dp + row);
-      zf[r] = a.z ? IO::load(zp + row) : 0.0f;
+      xf[r] = IO::load(xp + b * a.sx + d);
+      draw[r] = IO::load(dp + b * a.sd + d);
+      zf[r] = a.z ? IO::load(zp + b * a.sz + d) : 0.0f;
       const float* hp = a.state + row * N + sub * SPL;
       if constexpr (SPL == 4) {
         const float4 v = *reinterpret_cast<const float4*>(hp);
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a
 #pragma unroll
         for (int k = 0; k < SPL; ++k) h[r][k] = hp[k];
       }
-      const int64_t bg = (b * a.ngroups + d / a.group_dim) * N;  // (b, group of d)
+      const int64_t bg = b * a.sbc + d / a.group_dim * N;  // (b, group of d)
       const raw* Bt = static_cast<const raw*>(a.B) + bg + sub * SPL;
       const raw* Ct = static_cast<const raw*>(a.C) + bg + sub * SPL;
 #pragma unroll
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(DecodeKernelArgs a
         if (sub == 0) {
           if (a.D) y = fmaf(Dd, xf[r], y);
           if (a.z) y *= silu_f(zf[r]);
-          static_cast<raw*>(a.out)[row] = IO::from_f32(y);
+          static_cast<raw*>(a.out)[b * a.so + d] = IO::from_f32(y);
         }
       }
     }
@@ -156,6 +158,11 @@ hipError_t launch_typed(const DecodeProblem& p, hipStream_t stream) {
   a.dim = p.dim;
   a.ngroups = p.ngroups;
   a.group_dim = p.dim / p.ngroups;
+  a.sx = p.sx;
+  a.sd = p.sd;
+  a.sz = p.sz;
+  a.so = p.so;
+  a.sbc = p.sbc;
   const int64_t threads = p.dim * LPR;
   const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock),
                   static_cast<unsigned>((p.batch + kDecodeRows - 1) / kDecodeRows));

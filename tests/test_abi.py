@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
                           "mamba_state_update", "mamba_status_string", "mamba_last_error",
                           "mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd",
                           "mamba_scan_bwd_workspace_size", "mamba_ssd_fwd",
-                          "mamba_ssd_workspace_size"}
+                          "mamba_ssd_workspace_size", "mamba_scan_fwd_strided",
+                          "mamba_scan_workspace_size_strided", "mamba_state_update_strided"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -382,3 +383,69 @@ def test_ssd_validation(lib):
     assert ssd(lib, d, ws=40, ws_bytes=need, B=odd) == INVALID          # B needs 16 bytes
     assert "aligned" in err(lib)
     assert lib.mamba_ssd_workspace_size(ctypes.byref(S(headdim=32))) == 0
+
+
+def ST(**kw):
+    return bd.Strides(*(kw.get(k, 0) for k in ("x", "delta", "z", "out", "bc")))
+
+
+def scan_strided(lib, desc, strides, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, h0=None, out=9,
+                 last=10, ws=None, ws_bytes=0):
+    args = [x, delta, A, B, C, D, z, bias, h0, out, last]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    w = None if ws is None else (P(ws) if isinstance(ws, int) else ws)
+    return lib.mamba_scan_fwd_strided(ctypes.byref(desc), None if strides is None else ctypes.byref(strides),
+                                      *ptrs, w, ctypes.c_size_t(ws_bytes), None)
+
+
+def upd_strided(lib, desc, strides, state=11, x=1, delta=2, A=3, B=4, C=5, D=6, z=7, bias=8, out=9):
+    args = [state, x, delta, A, B, C, D, z, bias, out]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    return lib.mamba_state_update_strided(ctypes.byref(desc), ctypes.byref(strides), *ptrs, None)
+
+
+def test_strided_validation(lib):
+    d = D_()                                                # dim 16, N 16, bf16
+    assert scan_strided(lib, d, ST(x=15)) == INVALID        # below the row length
+    assert "x stride 15" in err(lib)
+    assert scan_strided(lib, d, ST(z=8)) == INVALID
+    assert scan_strided(lib, d, ST(bc=8)) == INVALID        # B/C rows hold G * N = 16
+    assert "bc stride" in err(lib)
+    assert scan_strided(lib, d, ST(out=1 << 27)) == UNSUPPORTED
+    assert scan_strided(lib, d, ST(bc=17)) == INVALID       # bf16 B/C rows must stay 4-byte aligned
+    assert "B/C rows" in err(lib)
+    # out's rows interleaved with x's: the spans overlap
+    base = FAKE + 0x100000 * 20
+    assert scan_strided(lib, d, ST(x=32, out=32), x=ctypes.c_void_p(base),
+                        out=ctypes.c_void_p(base + 32)) == INVALID
+    assert "out overlaps x" in err(lib)
+    # an input wider than its rows reaches further: last_state right after x's first rows
+    assert scan_strided(lib, d, ST(x=4096), x=ctypes.c_void_p(base),
+                        last=ctypes.c_void_p(base + 64 * 1024)) == INVALID
+    assert "last_state overlaps x" in err(lib)
+    # the common checks run under this entry point's name
+    assert scan_strided(lib, D_(dstate=5), None) == UNSUPPORTED
+    assert "mamba_scan_fwd_strided" in err(lib)
+
+
+def test_strided_workspace_size(lib):
+    long = D_(batch=64, seqlen=1 << 18, dim=4096)   # enough channel tiles for one or two segments
+    plain = lib.mamba_scan_workspace_size(ctypes.byref(long))
+    assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), None) == plain
+    assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), ctypes.byref(ST())) == plain
+    # wider rows keep every in-segment offset within 31 bits with more segments
+    assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), ctypes.byref(ST(x=65536))) > plain
+    assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), ctypes.byref(ST(x=5))) == 0
+
+
+def test_state_update_strided_validation(lib):
+    d = D_(seqlen=1)
+    assert upd_strided(lib, d, ST(delta=3)) == INVALID
+    assert "delta stride" in err(lib)
+    assert upd_strided(lib, d, ST(bc=15)) == INVALID
+    assert upd_strided(lib, D_(seqlen=2), ST()) == INVALID
+    assert "mamba_state_update_strided" in err(lib)
+    base = FAKE + 0x100000 * 20
+    assert upd_strided(lib, d, ST(x=64, out=64), x=ctypes.c_void_p(base),
+                       out=ctypes.c_void_p(base + 64)) == INVALID
+    assert "out overlaps x" in err(lib)
