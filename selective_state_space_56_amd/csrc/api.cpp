@@ -343,7 +343,7 @@ mamba_status state_update_impl(const char* who, const mamba_scan_desc* d,
   const int64_t G = groups_of(d);
   if (d->seqlen != 1)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: seqlen must be 1 (got %lld)", who, (long long)d->seqlen);
-  if ((d->batch + 15) / 16 > 65535)
+  if ((d->batch + 3) / 4 > 65535)   // grid rows of four batch rows
     return fail(MAMBA_ERR_UNSUPPORTED, "%s: batch %lld too large", who, (long long)d->batch);
   Rows rs;
   if ((st = resolve_rows(strides, d, who, rs)) != MAMBA_OK) return st;

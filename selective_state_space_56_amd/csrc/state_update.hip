@@ -24,8 +24,8 @@ namespace mscan {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kDecodeRows = 16;  // batch rows per thread
-constexpr int kGroupRows = 4;    // rows whose loads are in flight together
+constexpr int kDecodeRows = 4;   // batch rows per thread (fewer rows, more workgroups: measured best)
+constexpr int kGroupRows = 2;    // rows whose loads are in flight together
 
 struct DecodeKernelArgs {
   float* state;
