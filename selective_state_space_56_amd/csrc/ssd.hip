@@ -318,11 +318,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scores_kernel(const uint16
 // ---------------------------------------------------------------------------
 // 3. Chunk scan. Grid (chunks, heads, batch), eight waves. The chunk's X
 // (step-major) and the state it inherits (S_in, split into a bf16 pair hi + lo,
-// [p][n]) are staged in LDS once per workgroup. Wave w computes the output rows of the
-// 32-step tile w for both 32-channel tiles of p:
+// [p][n]) are staged in LDS once per workgroup. Each wave computes the output
+// rows of one 32-step tile for both 32-channel tiles of p:
 //   inherited part: C_t S_in (K = n; S_in as its pair hi + lo), rows scaled by
 //     exp(ell_t);
-//   diagonal part, per 32-step tile j <= w of earlier steps s: the chunk's
+//   diagonal part, per 32-step tile j <= i of earlier steps s: the chunk's
 //     scores B_s . C_t (a 32 x 32 tile with s as rows, from 3a, the next tile's
 //     load issued before the current one is used), masked (s <= t) and scaled
 //     by exp(ell_t - ell_s) Delta_s, taken off the diagonal as
@@ -331,9 +331,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scores_kernel(const uint16
 //     LDS) and formed directly on the diagonal tile, turned into the A operand
 //     (t as rows, s as k) by exchanging register halves across the half-waves,
 //     times X (K = s, transposing LDS reads);
-//   then + D x and one bf16 store per element.
-// The waves' work grows with w (1 to 8 score tiles); two workgroups per compute
-// unit keep its SIMDs busy meanwhile.
+//   then + D x; the 32 x 64 output tile leaves through LDS as 16-byte row
+//   stores.
+// Tile i takes i + 1 score tiles; waves are paired on SIMDs so that each SIMD
+// gets 9, and two workgroups per compute unit fill the gaps.
 constexpr int kScanThreads = 2 * kQ;
 
 __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
@@ -408,7 +409,9 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
   };
 
   {
-    const int i = wv;  // this wave's 32-step tile
+    // this wave's 32-step tile: waves w and w + 4 share a SIMD, so they take
+    // tiles w and 7 - w (9 score tiles per SIMD)
+    const int i = wv < 4 ? wv : 11 - wv;
     const int64_t t_row = t_base + 32 * i + lo;  // the step of this lane's C row
     // C fragments: the 8 bf16 at state offset 8 * hi + 16 kb of row t (rows past
     // the end load the last row and are zeroed)
