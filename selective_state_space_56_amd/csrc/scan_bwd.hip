@@ -357,7 +357,9 @@ __device__ __forceinline__ bool tile_path(uint32_t* flags, const float* A, int64
 
 // Checkpoint layout: float[chunk][N / 4][rows][4] (N >= 4) or
 // float[chunk][N][rows]: the state before the chunk's first step, for every
-// chunk of kChunk steps of the sequence.
+// chunk of kChunk steps of the sequence. Written once and read once, so the
+// 16-byte accesses are non-temporal.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <int N>
 __device__ __forceinline__ void ck_store(float* ck, int64_t chunk, int64_t rows, int64_t row,
                                          const float (&v)[N]) {
@@ -365,8 +367,8 @@ __device__ __forceinline__ void ck_store(float* ck, int64_t chunk, int64_t rows,
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int q = 0; q < N / 4; ++q)
-      *reinterpret_cast<float4*>(base + (q * rows + row) * 4) =
-          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      __builtin_nontemporal_store(f32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]},
+                                  reinterpret_cast<f32x4_t*>(base + (q * rows + row) * 4));
   } else {
 #pragma unroll
     for (int n = 0; n < N; ++n) base[n * rows + row] = v[n];
@@ -380,11 +382,12 @@ __device__ __forceinline__ void ck_load(const float* ck, int64_t chunk, int64_t 
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
-      const float4 w = *reinterpret_cast<const float4*>(base + (q * rows + row) * 4);
-      v[4 * q] = w.x;
-      v[4 * q + 1] = w.y;
-      v[4 * q + 2] = w.z;
-      v[4 * q + 3] = w.w;
+      const f32x4_t w =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(base + (q * rows + row) * 4));
+      v[4 * q] = w[0];
+      v[4 * q + 1] = w[1];
+      v[4 * q + 2] = w[2];
+      v[4 * q + 3] = w[3];
     }
   } else {
 #pragma unroll

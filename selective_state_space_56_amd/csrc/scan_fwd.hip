@@ -299,13 +299,15 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   // inputs of the chunk at step t1 into buffer nb (copies in flight, or held
   // in registers on the register-staged path until land() writes them)
   TileRegs<IO> rgx, rgd, rgz;
+  // the output pass is the last reader of x, Delta_raw and z: non-temporal
+  constexpr int kDmaAux = MODE == kOutput ? kNonTemporal : 0;
   auto fetch = [&](int nb, uint32_t t1) {
     const int64_t at = static_cast<int64_t>(t1);
     const uint32_t left = steps - t1;
     if constexpr (CW != 0) {
-      dma_tile<IO, CW>(x0 + at * g.sx, left, rbx, &st.in[nb][0][0][0], wv, lo_x);
-      dma_tile<IO, CW>(dl0 + at * g.sd, left, rbd, &st.in[nb][1][0][0], wv, lo_d);
-      if (kZ) dma_tile<IO, CW>(z0 + at * g.sz, left, rbz, &st.in[nb][kZi][0][0], wv, lo_z);
+      dma_tile<IO, CW, kDmaAux>(x0 + at * g.sx, left, rbx, &st.in[nb][0][0][0], wv, lo_x);
+      dma_tile<IO, CW, kDmaAux>(dl0 + at * g.sd, left, rbd, &st.in[nb][1][0][0], wv, lo_d);
+      if (kZ) dma_tile<IO, CW, kDmaAux>(z0 + at * g.sz, left, rbz, &st.in[nb][kZi][0][0], wv, lo_z);
     } else {
       load_tile_regs<IO>(rgx, x0 + at * g.sx, left, rbx, ch_off);
       load_tile_regs<IO>(rgd, dl0 + at * g.sd, left, rbd, ch_off);

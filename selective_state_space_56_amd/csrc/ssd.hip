@@ -205,7 +205,9 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunk_state_kernel(
     chunk_decay_from(dt_raw, dt_valid, bias, A_h, s_delta, s_ell, s_wave);
     if (c + 1 < g.chunks) dt_raw = load_dt(dt, g, b, h, c + 1, dt_valid);
     const float ell_last = s_ell[kQ - 1];
-    // the state entering this chunk (the row offset of register r is a constant)
+    // the state entering this chunk (the row offset of register r is a
+    // constant); non-temporal (aux 2): it is read once, by the chunk scan, and
+    // should not push the inputs read again out of the caches
     {
       const auto rs = make_rsrc(Sin + (bh * g.chunks + c) * per_head, per_head * 4);
       const uint32_t voff = static_cast<uint32_t>((4 * hi * kN + n) * 4);
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunk_state_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[pt][r]), rs, voff,
-                                                (pt * 32 + 8 * (r >> 2) + (r & 3)) * kN * 4, 0);
+                                                (pt * 32 + 8 * (r >> 2) + (r & 3)) * kN * 4, 2);
     }
     f32x16 acc[2] = {};
 #pragma unroll
@@ -375,7 +377,8 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
   const int64_t sin_off = (((b * g.nheads + h) * g.chunks + c) * kP) * kN;
 #pragma unroll
   for (int k = 0; k < kSPieces; ++k)
-    sv[k] = *reinterpret_cast<const f32x4*>(Sin + sin_off + (tid + kScanThreads * k) * 4);
+    sv[k] = __builtin_nontemporal_load(  // read once
+        reinterpret_cast<const f32x4*>(Sin + sin_off + (tid + kScanThreads * k) * 4));
   chunk_decay(dt, dt_bias ? dt_bias[h] : 0.0f, A[h], g, b, h, c, s_delta, s_ell, s_wave);
   // per step s: exp(ell_ref - ell_s) Delta_s, ell_ref at the end of the step's 32-step tile
   if (tid < kQ) s_v[tid] = hw_exp2((s_ell[tid | 31] - s_ell[tid]) * kLog2e) * s_delta[tid];
@@ -518,9 +521,9 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
     } else {
       diag(bufA);
     }
-    // epilogue: + D x into this wave's output tile in LDS, then 16-byte stores
-    // of whole rows through a buffer resource that ends with the sequence
-    // (rows past its end are dropped)
+    // epilogue: + D x into this wave's output tile in LDS, then 16-byte
+    // non-temporal stores of whole rows through a buffer resource that ends
+    // with the sequence (rows past its end are dropped)
     uint16_t* yt = &s_st[0][0][0] + wv * 32 * kP;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
@@ -540,7 +543,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
       const int id = lane + 64 * k, row = id >> 3, col = 8 * (id & 7);
       const u16x8 v = *reinterpret_cast<const u16x8*>(yt + row * kP + col);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc,
-                                             static_cast<uint32_t>(row * row_bytes + col * 2), 0, 0);
+                                             static_cast<uint32_t>(row * row_bytes + col * 2), 0, 2);
     }
   }
 }

@@ -54,7 +54,11 @@ __device__ __forceinline__ uint32_t tile_lane_offset(uint32_t row_bytes, uint32_
 // `rows`): rows past the segment read as zero, as do pieces past the last
 // channel (`lane_off`); they are never used. Lane i of wave `wv` lands S * i
 // bytes after the wave's LDS base.
-template <class IO, int S>
+// Cache policy of memory operations whose data is not read again by the
+// library (buffer instructions' aux field, gfx950: non-temporal).
+constexpr int kNonTemporal = 2;
+
+template <class IO, int S, int AUX = 0>
 __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t rows_left,
                                          uint32_t row_bytes, typename IO::raw* tile, int wv,
                                          uint32_t lane_off) {
@@ -71,16 +75,17 @@ __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t 
     const auto r = make_rsrc(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
     char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + wv * 64) * S;
     if constexpr (S == 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, lane_off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, lane_off, 0, 0, AUX);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, lane_off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, lane_off, 0, 0, AUX);
   }
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Write the y tile of one chunk from LDS to HBM in the pieces of dma_tile
-// (same per-instruction resources, so rows past the segment are dropped), or,
+// (same per-instruction resources, so rows past the segment are dropped;
+// non-temporal: outputs are not read again here), or,
 // with S == 0, each lane its own channel (`ch_off`, kOffNone past the last
 // channel) row by row.
 template <class IO, int S>
@@ -106,10 +111,11 @@ __device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows
       const auto r = make_rsrc(reinterpret_cast<char*>(rows) + r0 * row_bytes, left * row_bytes);
       const char* src = reinterpret_cast<const char*>(tile) + (k * kBlock + tid) * S;
       if constexpr (S == 16)
-        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, lane_off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src), r, lane_off, 0,
+                                               kNonTemporal);
       else
         __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(src), r, lane_off, 0,
-                                              0);
+                                              kNonTemporal);
     }
   }
 }
