@@ -88,3 +88,21 @@ def test_ssd_full_size_sampled_heads(orc, dev):
     inp = make_ssd_inputs(w, device=dev)
     heads = np.array([0, 1, 41, 79])
     _check(orc, inp, heads=heads, label="2.7B layer, sampled heads")
+
+
+def test_ssd_groups_with_h0_ragged(orc, dev):
+    """Two groups of heads, an initial state and a ragged last chunk at once."""
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"].with_shape(batch=2, seqlen=700, nheads=4, ngroups=2)
+    inp = make_ssd_inputs(w, device=dev, seed=9)
+    h0 = torch.randn((2, 4, w.dstate, w.headdim), generator=torch.Generator().manual_seed(8)).to(dev)
+    _check(orc, inp, h0=h0, label="groups + h0 + ragged")
+
+
+def test_ssd_deterministic(dev):
+    """Every sum is taken in a fixed order: two calls agree bit for bit."""
+    w = SSD_WORKLOADS["mamba2_2p7b_layer"].with_shape(batch=2, seqlen=1000, nheads=8)
+    inp = make_ssd_inputs(w, device=dev, seed=4)
+    a = ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"], dt_bias=inp["dt_bias"])
+    b = ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"], dt_bias=inp["dt_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
