@@ -78,13 +78,31 @@ typedef enum mamba_dtype {
 #define MAMBA_SCAN_ZOH (1u << 16)
 
 /*
+ * Kernel choice of mamba_scan_fwd (results agree to rounding either way).
+ * By default the segmented scan runs: one lane per (batch, channel) row with
+ * all N states in its registers; when there are too few rows to fill the GPU
+ * the sequence is cut into time segments (bits 0-15 of flags can force their
+ * number), which costs a second pass over the inputs and a workspace.
+ * MAMBA_SCAN_SPLIT_STATES selects the state-split scan instead: the 16 states
+ * of a row on four lanes, the whole sequence in one pass, no workspace
+ * (mamba_scan_workspace_size reports 0). It takes dstate 16 and the
+ * first-order input weight only, and rows (strides) of fewer than
+ * 2^31 / 9 bytes: otherwise MAMBA_ERR_UNSUPPORTED; with nonzero bits 0-15
+ * too, MAMBA_ERR_INVALID_ARG. It is not the default because it measured
+ * slower on the layers tried (0.45 against 0.38 ms on 8 x 2048 x 5120 bf16 on
+ * an MI355X, and no faster from 2 to 16 sequences).
+ */
+#define MAMBA_SCAN_SPLIT_STATES (1u << 17)
+
+/*
  * Problem sizes. dstate (N) must be 1, 2, 4, 8 or 16.
  * flags: for mamba_scan_fwd, bits 0-15 force the number of time segments the
  * sequence is cut into (0 = the library's choice; results agree to rounding
  * for any value, and the workspace size depends on it); MAMBA_SCAN_ZOH selects
  * the exact zero-order-hold input weight for mamba_scan_fwd, mamba_scan_fwd_init
- * and mamba_state_update; all other bits, and bits 0-15 for mamba_state_update,
- * must be 0.
+ * and mamba_state_update; MAMBA_SCAN_SPLIT_STATES (full-sequence entry points
+ * only) forces the state-split kernel; all other bits, and bits 0-15 for
+ * mamba_state_update, must be 0.
  */
 typedef struct mamba_scan_desc {
   int64_t batch;   /* >= 0                                         */

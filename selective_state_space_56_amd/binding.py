@@ -196,10 +196,11 @@ def workspace_size(batch, seqlen, dim, dstate, io_dtype=torch.bfloat16, segments
 
 
 ZOH_FLAG = 1 << 16  # MAMBA_SCAN_ZOH
+SPLIT_FLAG = 1 << 17  # MAMBA_SCAN_SPLIT_STATES
 
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out=None,
-             last_state=None, return_last_state=True, segments=0, zoh=False):
+             last_state=None, return_last_state=True, segments=0, zoh=False, split_states=False):
     """Selective scan over full sequences.
 
     x, delta (Delta_raw), z: (batch, L, dim) float32 or bfloat16 on a GPU;
@@ -209,7 +210,9 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     (zeros; with h0 the call goes to mamba_scan_fwd_init). Returns
     (out, last_state) where out is (batch, L, dim) in x's dtype and last_state
     (batch, dim, N) float32 (None if not requested). ``segments`` > 0 forces
-    the number of time segments; ``zoh`` selects the exact zero-order-hold
+    the number of time segments (the segmented kernel); ``split_states``
+    forces the state-split kernel (MAMBA_SCAN_SPLIT_STATES: N = 16, no ZOH);
+    by default the library chooses; ``zoh`` selects the exact zero-order-hold
     input weight (MAMBA_SCAN_ZOH) instead of the first-order Delta B.
     x, delta, z, B, C and out may be column slices of wider tensors (rows of
     contiguous elements, equally spaced): then the call goes to
@@ -247,7 +250,8 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
-    d = Desc(batch, L, dim, N, _IO[io], int(segments) | (ZOH_FLAG if zoh else 0), G)
+    d = Desc(batch, L, dim, N, _IO[io],
+             int(segments) | (ZOH_FLAG if zoh else 0) | (SPLIT_FLAG if split_states else 0), G)
     strides = Strides(sx, sd, sz or 0, so, sb)
     if (sx, sd, sz or dim, so, sb) != (dim, dim, dim, dim, G * N):
         ws_bytes = int(lib.mamba_scan_workspace_size_strided(ctypes.byref(d), ctypes.byref(strides)))

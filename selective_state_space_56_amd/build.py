@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmamba_scan.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "scan_fwd.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip", "ssd.hip"]
+SOURCES = ["api.cpp", "scan_fwd.hip", "scan_split.hip", "scan_bwd.hip", "state_update.hip", "conv1d.hip", "ssd.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",

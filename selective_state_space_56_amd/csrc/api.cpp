@@ -15,6 +15,7 @@
 
 #include "conv.h"
 #include "kernels.h"
+#include "scan_split.h"
 
 namespace {
 
@@ -77,6 +78,17 @@ mamba_status check_desc(const mamba_scan_desc* d, const char* who) {
 }
 
 int forced_segments(const mamba_scan_desc* d) { return static_cast<int>(d->flags & 0xffffu); }
+
+constexpr uint32_t kFwdFlags = 0xffffu | MAMBA_SCAN_ZOH | MAMBA_SCAN_SPLIT_STATES;
+
+// MAMBA_SCAN_SPLIT_STATES: 0 not asked for, 1 asked for and applicable, -1
+// asked for what the state-split kernel does not do.
+int split_mode(const mamba_scan_desc* d, int64_t row_elems) {
+  if (!(d->flags & MAMBA_SCAN_SPLIT_STATES)) return 0;
+  const bool fits = !(d->flags & MAMBA_SCAN_ZOH) && forced_segments(d) == 0 &&
+                    mscan::scan_split_fits(d->dstate, row_elems, d->io_dtype);
+  return fits ? 1 : -1;
+}
 
 int64_t groups_of(const mamba_scan_desc* d) { return d->ngroups > 1 ? d->ngroups : 1; }
 
@@ -159,10 +171,12 @@ const char* mamba_last_error(void) { return g_last_error.c_str(); }
 size_t mamba_scan_workspace_size_strided(const mamba_scan_desc* d, const mamba_scan_strides* s) {
   const char* who = "mamba_scan_workspace_size";
   if (check_desc(d, who) != MAMBA_OK) return 0;
-  if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH)) return 0;
+  if (d->flags & ~kFwdFlags) return 0;
   if (check_groups(d, who, true) != MAMBA_OK) return 0;
   Rows r;
   if (resolve_rows(s, d, who, r) != MAMBA_OK) return 0;
+  const int split = split_mode(d, widest(r));
+  if (split != 0) return 0;  // the state-split kernel needs none
   return mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
                           forced_segments(d), widest(r))
       .workspace_bytes;
@@ -184,9 +198,8 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
                            void* stream) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
-  if (d->flags & ~(0xffffu | MAMBA_SCAN_ZOH))
-    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who,
-                d->flags & ~(0xffffu | MAMBA_SCAN_ZOH));
+  if (d->flags & ~kFwdFlags)
+    return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~kFwdFlags);
   if ((st = check_groups(d, who, true)) != MAMBA_OK) return st;
   Rows rs;
   if ((st = resolve_rows(strides, d, who, rs)) != MAMBA_OK) return st;
@@ -205,8 +218,19 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
     if (!C) return fail(MAMBA_ERR_INVALID_ARG, "%s: C is NULL", who);
     if (!out) return fail(MAMBA_ERR_INVALID_ARG, "%s: out is NULL", who);
   }
-  const mscan::ScanPlan plan = mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
-                                                forced_segments(d), widest(rs));
+  if ((d->flags & MAMBA_SCAN_SPLIT_STATES) && forced_segments(d) > 0)
+    return fail(MAMBA_ERR_INVALID_ARG,
+                "%s: MAMBA_SCAN_SPLIT_STATES and a forced number of segments exclude each other", who);
+  const int split = split_mode(d, widest(rs));
+  if (split < 0)
+    return fail(MAMBA_ERR_UNSUPPORTED,
+                "%s: MAMBA_SCAN_SPLIT_STATES needs dstate 16, the first-order input weight and "
+                "rows of at most %lld bytes",
+                who, (long long)((int64_t(1) << 31) / 9 - 1));
+  mscan::ScanPlan plan{d->seqlen, 1, 0};
+  if (split == 0)
+    plan = mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
+                            forced_segments(d), widest(rs));
   if (elems > 0 && plan.workspace_bytes > 0) {
     if (!workspace)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who,
@@ -289,7 +313,10 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
   p.sz = rs.z;
   p.so = rs.o;
   p.sbc = rs.bc;
-  const hipError_t e = mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      split == 1 && p.seqlen > 0
+          ? mscan::launch_scan_split(p, static_cast<hipStream_t>(stream))
+          : mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

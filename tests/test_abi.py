@@ -118,7 +118,7 @@ def test_scan_rejects_bad_descriptors(lib):
     for n in (3, 5, 32, 64):
         assert scan(lib, D_(dstate=n)) == UNSUPPORTED
         assert "dstate" in err(lib)
-    assert scan(lib, D_(flags=1 << 17)) == INVALID
+    assert scan(lib, D_(flags=1 << 18)) == INVALID
     assert scan(lib, D_(batch=1 << 20, dim=1 << 20)) == UNSUPPORTED
 
 
@@ -313,8 +313,8 @@ def test_zoh_flag_validation(lib):
     d = D_(batch=1, seqlen=64, dim=16)
     dz_ = D_(batch=1, seqlen=64, dim=16, flags=ZOH)
     assert lib.mamba_scan_workspace_size(ctypes.byref(dz_)) == lib.mamba_scan_workspace_size(ctypes.byref(d))
-    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(flags=1 << 17))) == 0
-    assert scan(lib, D_(flags=1 << 17)) == INVALID
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(flags=1 << 18))) == 0
+    assert scan(lib, D_(flags=1 << 18)) == INVALID
     assert "unknown flag bits" in err(lib)
     assert upd(lib, D_(seqlen=1, flags=ZOH | 3)) == INVALID
     assert "MAMBA_SCAN_ZOH" in err(lib)
@@ -436,6 +436,36 @@ def test_strided_workspace_size(lib):
     # wider rows keep every in-segment offset within 31 bits with more segments
     assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), ctypes.byref(ST(x=65536))) > plain
     assert lib.mamba_scan_workspace_size_strided(ctypes.byref(long), ctypes.byref(ST(x=5))) == 0
+
+
+SPLIT = 1 << 17
+
+
+def test_split_flag_validation(lib):
+    """MAMBA_SCAN_SPLIT_STATES forces the state-split kernel: it needs no
+    workspace, takes dstate 16 and the first-order weight only, and excludes a
+    forced number of segments; the decode and backward calls reject it."""
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(batch=1, seqlen=64, dim=16, flags=SPLIT))) == 0
+    assert lib.mamba_scan_workspace_size(ctypes.byref(D_(dstate=8, flags=SPLIT))) == 0
+    assert scan(lib, D_(dstate=8, flags=SPLIT)) == UNSUPPORTED
+    assert "MAMBA_SCAN_SPLIT_STATES" in err(lib)
+    assert scan(lib, D_(flags=SPLIT | ZOH)) == UNSUPPORTED
+    assert scan(lib, D_(flags=SPLIT | 3)) == INVALID
+    assert "exclude" in err(lib)
+    assert upd(lib, D_(seqlen=1, flags=SPLIT)) == INVALID
+    assert bwd(lib, D_(batch=1, seqlen=64, dim=16, flags=SPLIT), ws=40, ws_bytes=1 << 20) == INVALID
+    # rows so wide that 9 steps of them pass 2^31 bytes: not for the split kernel
+    assert scan_strided(lib, D_(flags=SPLIT), ST(x=1 << 27)) == UNSUPPORTED
+
+
+def test_split_is_opt_in(lib):
+    """The segmented kernel is the default (it cuts a long sequence over few
+    rows into segments and asks for a workspace); the flag switches to the
+    state-split kernel, which asks for none."""
+    ws = lambda **k: lib.mamba_scan_workspace_size(ctypes.byref(D_(**k)))
+    for shape in (dict(batch=8, seqlen=2048, dim=5120), dict(batch=1, seqlen=2048, dim=5120)):
+        assert ws(**shape) > 0
+        assert ws(**shape, flags=SPLIT) == 0
 
 
 def test_state_update_strided_validation(lib):
