@@ -18,7 +18,8 @@ same run, each with its own roofline: the backward call on the same layer
 (`bwd`), the decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32
 state, `decode`), the causal convolution front-end (`conv`) and the Mamba-2
 SSD layer (80 heads of 64, N = 128, 8 x 2048, `ssd`, against the bf16
-matrix-core peak).
+matrix-core peak), and the same forward scan through the opt-in state-split
+kernel (`fwd_split`), for comparison with the default kernel.
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ KERNEL_SOURCES = {
     "conv_update": ["conv1d.hip", "device_math.h", "conv.h"],
     "bwd": ["scan_bwd.hip", "scan_fwd.hip", "tile_io.h", "device_math.h", "kernels.h"],
     "ssd": ["ssd.hip", "device_math.h", "kernels.h"],
+    "split": ["scan_split.hip", "scan_split.h", "tile_io.h", "device_math.h", "kernels.h"],
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
@@ -244,7 +246,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
-    ap.add_argument("--parts", default="fwd,bwd,decode,conv,ssd",
+    ap.add_argument("--parts", default="fwd,bwd,decode,conv,ssd,split",
                     help="comma list of the parts to run (profiling runs take one family at a time); "
                          "without fwd only the other parts' objects are printed")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -297,6 +299,8 @@ def main():
         rec["conv"] = conv_part(args, w, stream)
     if "ssd" in parts and not args.no_ssd:
         rec["ssd"] = ssd_part(args, stream)
+    if "split" in parts:
+        rec["fwd_split"] = split_part(args, w, inp, stream)
     if run_fwd and not args.no_cpu_baseline:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
         rec["cpu_baseline"] = cpu_baseline(w, inp, nthreads)
@@ -527,6 +531,37 @@ def ssd_part(args, stream):
     }
     del si, out, last
     return res
+
+
+def split_part(args, w, inp, stream):
+    """The same forward scan through the opt-in state-split kernel
+    (MAMBA_SCAN_SPLIT_STATES): timed beside the default for comparison."""
+    import torch
+    from selective_state_space_56_amd import scan_fwd
+    dev = inp["x"].device
+    out = torch.empty((w.batch, w.seqlen, w.dim), dtype=w.torch_io, device=dev)
+    last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def step():
+        scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                 delta_bias=inp["delta_bias"], out=out, last_state=last, split_states=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    calls = time_calls(step, args.steps, stream)
+    ms = sum(calls) / len(calls)
+    fl, by = scan_flops(w), scan_bytes(w)
+    return {
+        "op": "mamba_scan_fwd with MAMBA_SCAN_SPLIT_STATES (one scan_split_kernel launch; not the default)",
+        "workload": w.name, "avg_launch_ms": ms, **call_stats(calls),
+        "value": w.elem_steps / (ms * 1e-3), "unit": "elem-steps/s",
+        "roofline": {"bound": "alu", "achieved": fl / (ms * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fl / (ms * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+                     "traffic": recorded_traffic("split", w.name), "algorithmic_flops_per_launch": fl},
+        "hbm": {"achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": by},
+    }
 
 
 if __name__ == "__main__":

@@ -89,7 +89,7 @@ typedef enum mamba_dtype {
  * first-order input weight only, and rows (strides) of fewer than
  * 2^31 / 9 bytes: otherwise MAMBA_ERR_UNSUPPORTED; with nonzero bits 0-15
  * too, MAMBA_ERR_INVALID_ARG. It is not the default because it measured
- * slower on the layers tried (0.45 against 0.38 ms on 8 x 2048 x 5120 bf16 on
+ * slower on the layers tried (0.43 against 0.37-0.39 ms on 8 x 2048 x 5120 bf16 on
  * an MI355X, and no faster from 2 to 16 sequences).
  */
 #define MAMBA_SCAN_SPLIT_STATES (1u << 17)
