@@ -198,6 +198,20 @@ def test_split_run_twice_bitwise(dev):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_split_empty_sequence(dev):
+    """L = 0 with the flag: nothing to scan; the final state is h0, or zeros."""
+    w = WORKLOADS["mamba130m_layer"].with_shape(name="split_empty", batch=2, seqlen=0, dim=70)
+    inp = to_dev(make_scan_inputs(w, seed=2), dev)
+    h0 = make_decode_state(w, device=dev, seed=2)
+    out, last = _split(inp, h0=h0)
+    assert out.shape == (2, 0, 70) and torch.equal(last, h0)
+    last0 = torch.full((2, 70, 16), 7.0, device=dev)
+    scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+             delta_bias=inp["delta_bias"], last_state=last0, split_states=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(last0).item() == 0
+
+
 def test_split_rejects_unsupported(dev):
     w = WORKLOADS["mamba130m_layer"].with_shape(name="split_bad", batch=1, seqlen=16, dim=64, dstate=8)
     inp = to_dev(make_scan_inputs(w, seed=1), dev)
