@@ -316,7 +316,8 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
   const hipError_t e =
       split == 1 && p.seqlen > 0
           ? mscan::launch_scan_split(p, static_cast<hipStream_t>(stream))
-          : mscan::launch_scan_fwd(p, plan, workspace, static_cast<hipStream_t>(stream));
+          : mscan::launch_scan_fwd(p, plan, plan.workspace_bytes > 0 ? workspace : nullptr,
+                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(MAMBA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();

@@ -515,7 +515,10 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.sz = p.z ? p.sz : p.sx;
   g.so = p.so;
   g.sbc = p.sbc;
-  float* ws_h = static_cast<float*>(workspace);
+  // The workspace (segment aggregates, then the tile flags) exists only with
+  // more than one segment; a single-segment plan ignores any buffer passed
+  // in, so no kernel reads flags that this call did not write.
+  float* ws_h = plan.segments > 1 ? static_cast<float*>(workspace) : nullptr;
   float* ws_s = ws_h ? ws_h + static_cast<int64_t>(plan.segments - 1) * g.rows * N : nullptr;
   g.tile_flags = ws_s ? reinterpret_cast<uint32_t*>(ws_s + static_cast<int64_t>(plan.segments - 1) *
                                                                g.rows)

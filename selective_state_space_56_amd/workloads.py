@@ -255,3 +255,57 @@ def to_f64_numpy(t):
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# Steps at which make_edge_inputs places runs of exact zeros in x: each run is
+# at least 16 steps long, and together they cross the 8-step chunk edges and
+# the segment edges of 1, 4, 5 and 12 time segments at L = 600 (56, 112, 120,
+# 152, 168, 240, 304, 456, 480), plus one run that ends the sequence.
+EDGE_ZERO_RUNS = ((50, 70), (104, 130), (145, 175), (230, 262), (296, 312), (450, 500), (584, 600))
+
+
+def make_edge_inputs(w: Workload, device="cpu", seed=0):
+    """make_scan_inputs() moved into the regimes where a step size is large or
+    an input vanishes ("Mamba and selective state spaces, from first
+    principles", "Discretisation: zero-order hold": a large step wipes the
+    state; "Selection": a large step at a document boundary resets it):
+
+      channels d % 4 == 1: bias ~ U(3, 8) (every step large);
+      channels d % 4 == 2: bias ~ U(8, 20) (state wiped at every step);
+      channels d % 4 == 3: Delta_raw raised by U(10, 20) at about 2 % of the
+                           steps (isolated resets), bias unchanged;
+      channels d % 3 == 0: x exactly 0 on the runs EDGE_ZERO_RUNS;
+      channels d % 3 == 1: x = +-1e-39 (subnormal in fp32 and bf16) on steps
+                           300..339 and +-1e-30 on steps 340..359;
+      every channel:       x exactly 0 on steps 576..591.
+
+    Values are placed, never computed from the method; rounding to the io
+    dtype happens after placement, as in make_scan_inputs()."""
+    base = make_scan_inputs(w.with_shape(io="f32"), device=device, seed=seed)
+    g = _gen(device, seed + 424242)
+    x = base["x"].clone()
+    delta = base["delta"].clone()
+    bias = base["delta_bias"].clone()
+    L, dim = w.seqlen, w.dim
+    ch = torch.arange(dim, device=device)
+    m1, m2, m3 = ch % 4 == 1, ch % 4 == 2, ch % 4 == 3
+    bias[m1] = 3.0 + 5.0 * torch.rand(int(m1.sum()), generator=g, device=device)
+    bias[m2] = 8.0 + 12.0 * torch.rand(int(m2.sum()), generator=g, device=device)
+    spikes = torch.rand((w.batch, L, dim), generator=g, device=device) < 0.02
+    lift = 10.0 + 10.0 * torch.rand((w.batch, L, dim), generator=g, device=device)
+    delta = torch.where(spikes & m3, delta + lift, delta)
+    z0 = ch % 3 == 0
+    for a, b in EDGE_ZERO_RUNS:
+        a, b = min(a, L), min(b, L)
+        x[:, a:b, z0] = 0.0
+    tiny = ch % 3 == 1
+    sign = torch.where(torch.rand((w.batch, L, dim), generator=g, device=device) < 0.5, -1.0, 1.0)
+    for (a, b), mag in (((300, 340), 1e-39), ((340, 360), 1e-30)):
+        a, b = min(a, L), min(b, L)
+        x[:, a:b, tiny] = (sign[:, a:b] * mag)[:, :, tiny]
+    x[:, min(576, L):min(592, L), :] = 0.0
+    io = w.torch_io
+    out = {"x": x.to(io), "delta": delta.to(io), "B": base["B"].to(io), "C": base["C"].to(io),
+           "z": None if base["z"] is None else base["z"].to(io),
+           "A": base["A"], "D": base["D"], "delta_bias": bias}
+    return out
