@@ -38,9 +38,21 @@ def rocm_path() -> str:
     return os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-def _compile(src: str) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """Whether obj is older than src or any header under csrc/ or include/."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE)
+                                        for f in os.listdir(d) if f.endswith(".h")]
+    return any(os.path.getmtime(p) > t for p in deps)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
         cmd = [hipcc()] + COMMON + DEVICE + ["-c", path, "-o", obj]
@@ -53,10 +65,11 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library. Returns its path."""
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (with incremental=True only those newer than
+    their object) and link the shared library. Returns its path."""
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, incremental), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,5 +82,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

@@ -472,15 +472,25 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
           e[8 * q + r + 4] = __uint_as_float(w2[1]);
         }
       }
+      // the weights as a bf16 pair hi + lo (two products): one bf16 operand
+      // would round each weight by up to 2^-9, and a long-memory head sums
+      // hundreds of such terms into one output
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        u16x8 pk;
+        u16x8 pk, pl;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pk[k] = to_bf16(e[8 * q + k]);
+        for (int k = 0; k < 8; ++k) {
+          pk[k] = to_bf16(e[8 * q + k]);
+          pl[k] = to_bf16(e[8 * q + k] - from_bf16(pk[k]));
+        }
         const bf16x8 aop = __builtin_bit_cast(bf16x8, pk);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-          acc[pt] = mfma(aop, lds_kmajor(&s_x[32 * j + 16 * q][pt * 32], ldx, lane), acc[pt]);
+        for (int pt = 0; pt < 2; ++pt) {
+          const bf16x8 xop = lds_kmajor(&s_x[32 * j + 16 * q][pt * 32], ldx, lane);
+          acc[pt] = mfma(aop, xop, acc[pt]);
+          acc[pt] = mfma(alo, xop, acc[pt]);
+        }
       }
     };
     // tile j < i: every s precedes every t, both factors are at most 1

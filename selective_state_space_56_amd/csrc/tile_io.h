@@ -33,6 +33,13 @@ __device__ __forceinline__ void scaled_powers(float e, float rho, float (&p)[N])
 
 using lds_void = __attribute__((address_space(3))) void;
 
+// A value every lane of the wave holds: taken from the first lane, so that
+// the compiler keeps it (and what is built from it, like a buffer resource)
+// in scalar registers instead of looping over lanes to make it uniform.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Per-lane byte offset of a tile piece: a tile of kChunk rows (steps) by
 // kBlock channels is moved S bytes per lane, lane i of instruction k taking
 // the piece (k * kBlock + i) * S bytes into the tile; each instruction covers
@@ -58,12 +65,12 @@ __device__ __forceinline__ uint32_t tile_lane_offset(uint32_t row_bytes, uint32_
 // library (buffer instructions' aux field, gfx950: non-temporal).
 constexpr int kNonTemporal = 2;
 
-template <class IO, int S, int AUX = 0>
+template <class IO, int S, int AUX = 0, int KC = kChunk>
 __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t rows_left,
                                          uint32_t row_bytes, typename IO::raw* tile, int wv,
                                          uint32_t lane_off) {
   constexpr int eb = sizeof(typename IO::raw);
-  constexpr int kTileBytes = kChunk * kBlock * eb;
+  constexpr int kTileBytes = KC * kBlock * eb;
   constexpr int kPerInstr = kBlock * S;
   constexpr int kRowsPerInstr = S / eb;
   static_assert(kTileBytes % kPerInstr == 0, "tile must be a whole number of copies");
@@ -71,7 +78,8 @@ __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t 
 #pragma unroll
   for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
     const uint32_t r0 = k * kRowsPerInstr;
-    const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+    // wave-uniform; read into a scalar register so the resource is built there
+    const uint32_t left = uniform_u32(rows_left > r0 ? rows_left - r0 : 0u);
     const auto r = make_rsrc(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
     char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + wv * 64) * S;
     if constexpr (S == 16)
@@ -88,7 +96,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // non-temporal: outputs are not read again here), or,
 // with S == 0, each lane its own channel (`ch_off`, kOffNone past the last
 // channel) row by row.
-template <class IO, int S>
+template <class IO, int S, int KC = kChunk>
 __device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows_left,
                                            uint32_t row_bytes, const typename IO::raw* tile,
                                            uint32_t lane_off, uint32_t ch_off) {
@@ -97,17 +105,17 @@ __device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows
   if constexpr (S == 0) {
     const auto r = make_rsrc(rows);
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j)
+    for (int j = 0; j < KC; ++j)
       if (static_cast<uint32_t>(j) < rows_left)
         IO::bstore(tile[j * kBlock + tid], r, ch_off, j * row_bytes);
   } else {
-    constexpr int kTileBytes = kChunk * kBlock * eb;
+    constexpr int kTileBytes = KC * kBlock * eb;
     constexpr int kPerInstr = kBlock * S;
     constexpr int kRowsPerInstr = S / eb;
 #pragma unroll
     for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
       const uint32_t r0 = k * kRowsPerInstr;
-      const uint32_t left = rows_left > r0 ? rows_left - r0 : 0u;
+      const uint32_t left = uniform_u32(rows_left > r0 ? rows_left - r0 : 0u);
       const auto r = make_rsrc(reinterpret_cast<char*>(rows) + r0 * row_bytes, left * row_bytes);
       const char* src = reinterpret_cast<const char*>(tile) + (k * kBlock + tid) * S;
       if constexpr (S == 16)
@@ -124,25 +132,25 @@ __device__ __forceinline__ void store_tile(typename IO::raw* rows, uint32_t rows
 // (an odd number of bf16 channels): each lane loads its own channel's value
 // for every step of the chunk, and writes them to LDS after the current chunk
 // has been computed.
-template <class IO>
+template <class IO, int KC = kChunk>
 struct TileRegs {
-  typename IO::raw v[kChunk];
+  typename IO::raw v[KC];
 };
 
-template <class IO>
-__device__ __forceinline__ void load_tile_regs(TileRegs<IO>& tr, const typename IO::raw* rows,
+template <class IO, int KC>
+__device__ __forceinline__ void load_tile_regs(TileRegs<IO, KC>& tr, const typename IO::raw* rows,
                                                uint32_t rows_left, uint32_t row_bytes,
                                                uint32_t ch_off) {
   const auto r = make_rsrc(rows);
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j)
+  for (int j = 0; j < KC; ++j)
     tr.v[j] = IO::bload(r, static_cast<uint32_t>(j) < rows_left ? ch_off : kOffNone, j * row_bytes);
 }
 
-template <class IO>
-__device__ __forceinline__ void store_tile_regs(const TileRegs<IO>& tr, typename IO::raw* tile) {
+template <class IO, int KC>
+__device__ __forceinline__ void store_tile_regs(const TileRegs<IO, KC>& tr, typename IO::raw* tile) {
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) tile[j * kBlock + threadIdx.x] = tr.v[j];
+  for (int j = 0; j < KC; ++j) tile[j * kBlock + threadIdx.x] = tr.v[j];
 }
 
 // Thread i < kChunk * 2N fetches element i of a chunk's B/C tile: B or C of
@@ -152,11 +160,11 @@ __device__ __forceinline__ void store_tile_regs(const TileRegs<IO>& tr, typename
 struct BcOffsets {
   uint32_t b, c;
 };
-template <int N, class IO>
+template <int N, class IO, int KC = kChunk>
 __device__ __forceinline__ BcOffsets bc_offsets(int i, uint32_t row_elems) {
   constexpr int eb = sizeof(typename IO::raw);
   const int j = i / (2 * N), k = i % (2 * N);
-  const bool in_tile = i < kChunk * 2 * N;
+  const bool in_tile = i < KC * 2 * N;
   return {in_tile && k < N ? static_cast<uint32_t>((j * row_elems + k) * eb) : kOffNone,
           in_tile && k >= N ? static_cast<uint32_t>((j * row_elems + k - N) * eb) : kOffNone};
 }

@@ -67,10 +67,10 @@ def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=Tru
     def sl(t, dim_axis):
         if t is None:
             return None
-        a = to_f64_numpy(t)
-        if channels is not None:
-            a = np.take(a, channels, axis=dim_axis)
-        return a
+        if channels is not None:   # select on the tensor's device, then widen
+            idx = torch.as_tensor(np.asarray(channels), dtype=torch.long, device=t.device)
+            t = t.index_select(dim_axis, idx)
+        return to_f64_numpy(t)
     A = sl(inp["A"], 0)
     return orc.scan(sl(inp["x"], 2), sl(inp["delta"], 2), A, to_f64_numpy(inp["B"]),
                     to_f64_numpy(inp["C"]), D=sl(inp["D"], 0) if with_D else None,
@@ -82,3 +82,38 @@ def oracle_scan(orc, inp, channels=None, with_D=True, with_z=True, with_bias=Tru
 def gpu_decode(state, tok, params):
     return state_update(state, tok["x"], tok["delta"], params["A"], tok["B"], tok["C"],
                         D=params["D"], z=tok["z"], delta_bias=params["delta_bias"])
+
+
+class BlockedErr:
+    """norm_err over a tensor compared block by block (the oracle runs on
+    channel blocks to bound host memory): |g - r| and |r| of every block are
+    kept on the GPU (fp32) and the sum of r^2 in fp64, so the result is the
+    metric of the whole tensor, with the rms of all of it."""
+
+    def __init__(self):
+        self.d, self.a, self.ss, self.n = [], [], 0.0, 0
+        self.plain = 0.0
+
+    def add(self, got, ref):
+        g = torch.as_tensor(got).to("cuda", torch.float64)
+        r = torch.as_tensor(np.ascontiguousarray(ref)).to("cuda", torch.float64)
+        assert g.shape == r.shape, (g.shape, r.shape)
+        if not bool(torch.isfinite(g).all()):
+            raise AssertionError("non-finite output")
+        self.ss += float((r * r).sum())
+        self.n += r.numel()
+        self.d.append((g - r).abs().float())
+        self.a.append(r.abs().float())
+
+    def err(self) -> float:
+        if self.n == 0:
+            return 0.0
+        rms = (self.ss / self.n) ** 0.5
+        worst, plain = 0.0, 0.0
+        for d, a in zip(self.d, self.a):
+            worst = max(worst, float((d / (a + rms)).max()) if rms > 0 else float(d.max()))
+            big = a >= rms
+            if rms > 0 and bool(big.any()):
+                plain = max(plain, float((d[big] / a[big]).max()))
+        self.plain = plain
+        return worst
