@@ -258,6 +258,40 @@ mamba_status mamba_state_update_strided(const mamba_scan_desc *desc,
                                         const float *delta_bias, void *out,
                                         void *stream);
 
+/*
+ * mamba_scan_fwd_init for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace argument and allocates nothing (no
+ * hipMalloc, hipFree or allocating library call): the time segments' end
+ * states, Delta sums and tile flags go to a fixed array of
+ * MAMBA_SCAN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU the library
+ * runs on, held until the process ends. Its device address is looked up on
+ * the first call on each device (that call may load the library's code
+ * object onto the device; the caller may make one small call during
+ * set-up).
+ *  - Every call on a GPU shares that GPU's array: calls that overlap in time
+ *    on one GPU (different streams, without ordering between them) race and
+ *    give wrong results; order them on one stream or with events. Calls on
+ *    different GPUs are independent.
+ *  - Nothing needs clearing: every word a call reads from the array is
+ *    written earlier in the same call, in stream order.
+ *  - The library's own segment plan needs at most about 36 MB on a 256-CU
+ *    device; a plan that needs more than the array holds (a large forced
+ *    segment count in flags bits 0-15, or very long sequences whose byte
+ *    offsets force extra segments) returns MAMBA_ERR_UNSUPPORTED before any
+ *    HIP call, with the sizes in mamba_last_error(). MAMBA_ERR_HIP if the
+ *    array's address cannot be obtained.
+ * All other arguments, semantics, validation and results are those of
+ * mamba_scan_fwd_init (h0 may be NULL: zeros).
+ */
+#define MAMBA_SCAN_NOALLOC_SCRATCH_BYTES (48u << 20)
+mamba_status mamba_scan_fwd_noalloc(const mamba_scan_desc *desc, const void *x,
+                                    const void *delta, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const void *z, const float *delta_bias,
+                                    const float *h0, void *out,
+                                    float *last_state, void *stream);
+
 /* Static name of a status code ("MAMBA_OK", ...). */
 const char *mamba_status_string(int status);
 

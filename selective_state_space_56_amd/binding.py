@@ -81,6 +81,9 @@ def load_library(path: str = LIB_PATH):
         lib.mamba_scan_fwd.restype = ctypes.c_int
         lib.mamba_scan_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, vp, fp,
                                        vp, sz, vp]
+        lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.mamba_scan_fwd_noalloc.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp,
+                                               fp, vp, fp, vp]
         lib.mamba_scan_fwd_init.restype = ctypes.c_int
         lib.mamba_scan_fwd_init.argtypes = [ctypes.POINTER(Desc), vp, vp, fp, vp, vp, fp, vp, fp, fp,
                                             vp, fp, vp, sz, vp]
@@ -338,6 +341,44 @@ def scan_bwd(x, delta, A, B, C, dout, D=None, z=None, delta_bias=None, *, h0=Non
                             _ptr(g["dh0"]), _ptr(ws), ctypes.c_size_t(ws_bytes), _stream(dev))
     _check(lib, st)
     return g
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, delta_bias=None, *, h0=None, out=None,
+                     last_state=None, segments=0):
+    """scan_fwd through mamba_scan_fwd_noalloc: no workspace is allocated (the
+    library's fixed device scratch array is used). Contiguous tensors, shapes
+    and dtypes as scan_fwd; out and last_state are allocated here unless
+    given. Returns (out, last_state)."""
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, L, dim) and A (dim, N)")
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    dev = x.device
+    io = x.dtype
+    if dev.type != "cuda" or io not in _IO:
+        raise ValueError("scan_fwd_noalloc takes float32 or bfloat16 tensors on a GPU")
+    G = _groups(B)
+    bshape = (batch, L, G, N) if B.dim() == 4 else (batch, L, N)
+    for t, name, shp, dt in [(x, "x", (batch, L, dim), io), (delta, "delta", (batch, L, dim), io),
+                             (z, "z", (batch, L, dim), io), (B, "B", bshape, io),
+                             (C, "C", bshape, io), (A, "A", (dim, N), torch.float32),
+                             (D, "D", (dim,), torch.float32),
+                             (delta_bias, "delta_bias", (dim,), torch.float32),
+                             (h0, "h0", (batch, dim, N), torch.float32)]:
+        _need(t, name, shp, dt, dev)
+    if out is None:
+        out = torch.empty((batch, L, dim), dtype=io, device=dev)
+    if last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _need(out, "out", (batch, L, dim), io, dev)
+    _need(last_state, "last_state", (batch, dim, N), torch.float32, dev)
+    d = Desc(batch, L, dim, N, _IO[io], int(segments), G)
+    st = lib.mamba_scan_fwd_noalloc(ctypes.byref(d), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                    _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(h0), _ptr(out),
+                                    _ptr(last_state), _stream(dev))
+    _check(lib, st)
+    return out, last_state
 
 
 def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,

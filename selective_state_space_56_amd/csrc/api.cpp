@@ -190,12 +190,17 @@ size_t mamba_scan_workspace_size(const mamba_scan_desc* d) {
 
 namespace {
 
+static_assert(MAMBA_SCAN_NOALLOC_SCRATCH_BYTES == mscan::kScanScratchBytes,
+              "the header states the scratch array's size");
+
+// use_scratch: the allocation-free entry point (the workspace is the
+// library's fixed device array, not an argument).
 mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
                            const mamba_scan_strides* strides, const void* x, const void* delta,
                            const float* A, const void* B, const void* C, const float* D,
                            const void* z, const float* delta_bias, const float* h0, void* out,
                            float* last_state, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           void* stream, bool use_scratch = false) {
   mamba_status st = check_desc(d, who);
   if (st != MAMBA_OK) return st;
   if (d->flags & ~kFwdFlags)
@@ -231,7 +236,13 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
   if (split == 0)
     plan = mscan::plan_scan(d->batch, d->seqlen, d->dim, static_cast<int>(d->dstate),
                             forced_segments(d), widest(rs));
-  if (elems > 0 && plan.workspace_bytes > 0) {
+  if (use_scratch && elems > 0 && plan.workspace_bytes > mscan::kScanScratchBytes)
+    return fail(MAMBA_ERR_UNSUPPORTED,
+                "%s: this problem's segment plan needs %zu bytes of scratch, the library's fixed "
+                "device array holds %zu (force fewer time segments with flags bits 0-15, or call "
+                "mamba_scan_fwd_init with a workspace)",
+                who, plan.workspace_bytes, static_cast<size_t>(mscan::kScanScratchBytes));
+  if (!use_scratch && elems > 0 && plan.workspace_bytes > 0) {
     if (!workspace)
       return fail(MAMBA_ERR_INVALID_ARG, "%s: workspace is NULL but %zu bytes are needed", who,
                   plan.workspace_bytes);
@@ -256,7 +267,9 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
   };
   const Span o_out{"out", out, span_bytes(rowsteps, rs.o, d->dim, eb)};
   const Span o_last{"last_state", last_state, static_cast<size_t>(rows) * N * 4};
-  const Span o_ws{"workspace", elems > 0 ? workspace : nullptr, plan.workspace_bytes};
+  // (the fixed scratch array is the library's own: no caller buffer can overlap it)
+  const Span o_ws{"workspace", elems > 0 && !use_scratch ? workspace : nullptr,
+                  plan.workspace_bytes};
   for (const Span& s : in) {
     if (overlaps(o_out, s)) return fail(MAMBA_ERR_INVALID_ARG, "%s: out overlaps %s", who, s.name);
     if (overlaps(o_last, s))
@@ -288,6 +301,14 @@ mamba_status scan_fwd_impl(const char* who, const mamba_scan_desc* d,
       return fail(MAMBA_ERR_INVALID_ARG, "%s: an fp32 argument is not 4-byte aligned", who);
 
   if (rows == 0 || (elems == 0 && !last_state)) return ok();
+  if (use_scratch && elems > 0 && plan.workspace_bytes > 0) {
+    void* sp = nullptr;
+    const hipError_t se = mscan::scan_scratch(&sp);
+    if (se != hipSuccess)
+      return fail(MAMBA_ERR_HIP, "%s: the scratch array's device address: %s", who,
+                  hipGetErrorString(se));
+    workspace = sp;
+  }
 
   mscan::ScanProblem p;
   p.x = x;
@@ -352,6 +373,14 @@ mamba_status mamba_scan_fwd_strided(const mamba_scan_desc* d, const mamba_scan_s
                                     void* stream) {
   return scan_fwd_impl("mamba_scan_fwd_strided", d, strides, x, delta, A, B, C, D, z, delta_bias, h0,
                        out, last_state, workspace, workspace_bytes, stream);
+}
+
+mamba_status mamba_scan_fwd_noalloc(const mamba_scan_desc* d, const void* x, const void* delta,
+                                    const float* A, const void* B, const void* C, const float* D,
+                                    const void* z, const float* delta_bias, const float* h0,
+                                    void* out, float* last_state, void* stream) {
+  return scan_fwd_impl("mamba_scan_fwd_noalloc", d, nullptr, x, delta, A, B, C, D, z, delta_bias,
+                       h0, out, last_state, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

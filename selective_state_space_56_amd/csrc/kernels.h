@@ -49,6 +49,11 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
 hipError_t launch_scan_fwd(const ScanProblem& p, const ScanPlan& plan, void* workspace,
                            hipStream_t stream);
 
+// Bytes of the fixed device scratch array of the allocation-free entry point,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kScanScratchBytes = size_t(48) << 20;
+hipError_t scan_scratch(void** ptr);
+
 // The combine launch of launch_scan_fwd on its own: folds segment
 // aggregates ws_h[k][rows][dstate] (end state from zero) and ws_s[k][rows]
 // (sum of Delta), k < segments - 1, from h0 (or zero) in time order, leaving

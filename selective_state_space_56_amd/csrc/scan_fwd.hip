@@ -647,6 +647,36 @@ static int device_cus() {
 
 int device_cu_count() { return device_cus(); }
 
+// Fixed scratch of the allocation-free entry point (mamba_scan_fwd_noalloc):
+// the segment aggregates (end states, Delta sums) and tile flags of one call,
+// in a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends. Every word a call reads from it is written earlier
+// in the same call (aggregate launch, then fold, then output launch, all on
+// the caller's stream), so nothing needs clearing between calls; calls that
+// overlap in time on one GPU race on it. The library's own segment plan needs
+// at most about 36 MB on a 256-CU device (two rounds of output workgroups of
+// 256 channels, 68 bytes per channel and segment).
+static __device__ __align__(256) unsigned char scratch[kScanScratchBytes];
+
+hipError_t scan_scratch(void** ptr) {
+  // The array's host-side name is only a stand-in: kernels get the device
+  // address, looked up once per device with that device current.
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int forced_segments,
                    int64_t row_elems) {
   ScanPlan plan{seqlen, 1, 0};

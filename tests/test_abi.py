@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
                           "mamba_conv1d_fwd", "mamba_conv1d_update", "mamba_scan_bwd",
                           "mamba_scan_bwd_workspace_size", "mamba_ssd_fwd",
                           "mamba_ssd_workspace_size", "mamba_scan_fwd_strided",
-                          "mamba_scan_workspace_size_strided", "mamba_state_update_strided"}
+                          "mamba_scan_workspace_size_strided", "mamba_state_update_strided",
+                          "mamba_scan_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
 
@@ -479,3 +480,25 @@ def test_state_update_strided_validation(lib):
     assert upd_strided(lib, d, ST(x=64, out=64), x=ctypes.c_void_p(base),
                        out=ctypes.c_void_p(base + 64)) == INVALID
     assert "out overlaps x" in err(lib)
+
+
+def scan_noalloc(lib, desc, h0=None, out=9, last=10):
+    args = [1, 2, 3, 4, 5, 6, 7, 8, h0, out, last]
+    ptrs = [None if a is None else (P(a) if isinstance(a, int) else a) for a in args]
+    return lib.mamba_scan_fwd_noalloc(ctypes.byref(desc), *ptrs, None)
+
+
+def test_scan_noalloc_validation(lib):
+    """The allocation-free scan validates like mamba_scan_fwd_init, and a
+    segment plan larger than its fixed scratch array is refused (before any
+    HIP call) with the sizes in the message."""
+    d = D_()
+    assert scan_noalloc(lib, d, h0=9) == INVALID               # h0 == out
+    assert scan_noalloc(lib, d, out=None) == INVALID           # out missing
+    assert scan_noalloc(lib, D_(flags=1 << 20)) == INVALID     # unknown flag bit
+    big = D_(batch=4, seqlen=100000, dim=5120, flags=4000)     # 4000 forced segments
+    assert lib.mamba_scan_workspace_size(ctypes.byref(big)) > (48 << 20)
+    assert scan_noalloc(lib, big) == UNSUPPORTED
+    msg = lib.mamba_last_error().decode()
+    assert "scratch" in msg and str(48 << 20) in msg, msg
+    assert lib.mamba_scan_fwd_noalloc(None, *[P(k) for k in range(1, 12)], None) == INVALID
