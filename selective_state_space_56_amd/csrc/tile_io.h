@@ -53,18 +53,68 @@ __device__ __forceinline__ uint32_t tile_lane_offset(uint32_t row_bytes, uint32_
   return col + S <= valid_bytes ? row * row_bytes + col : kOffNone;
 }
 
-// Copy rows 0 .. kChunk - 1 (from `rows`, the tile's first element in the
-// chunk's first step) of one input tensor's channel tile straight from global
-// memory into LDS (buffer_load ... lds: no registers involved). Each copy
-// instruction gets its own buffer resource, built in scalar registers, that
-// starts at its first row and ends at the segment's end (`rows_left` rows from
-// `rows`): rows past the segment read as zero, as do pieces past the last
-// channel (`lane_off`); they are never used. Lane i of wave `wv` lands S * i
-// bytes after the wave's LDS base.
 // Cache policy of memory operations whose data is not read again by the
 // library (buffer instructions' aux field, gfx950: non-temporal).
 constexpr int kNonTemporal = 2;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One global-to-LDS copy instruction (buffer_load_dword{,x4} ... lds): lane i
+// of the wave reads S bytes at `voff` in the buffer described by `rsrc` and
+// writes them S * i bytes after `lds_base` (taken from M0).
+//
+// It is issued from inline assembly on purpose. The compiler tracks every
+// LDS copy it emits itself and, unable to tell the two staging buffers apart,
+// makes the next LDS access of any kind wait for all copies in flight
+// (vmcnt(0)), which turns the prefetch of the next chunk into a full memory
+// round trip at the start of every chunk. Copies it does not know about are
+// not tracked; their callers order them explicitly instead: wait_vmem()
+// (vmcnt(0)) and a workgroup barrier come between a copy and the first read
+// of its bytes, and no lane reads or writes the target buffer while a copy is
+// in flight. The instruction has no register results, so no register is
+// left pending when the statement ends. The compiler's own counter waits stay
+// correct: extra copies in flight only make them wait longer.
+template <int S, int AUX>
+__device__ __forceinline__ void lds_copy(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  static_assert(S == 16 || S == 4, "copies are 16 or 4 bytes per lane");
+  static_assert(AUX == 0 || AUX == kNonTemporal, "plain or non-temporal copies");
+  if constexpr (S == 16 && AUX == 0)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+  else if constexpr (S == 16)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc),
+                 "{m0}"(lds_base)
+                 : "memory");
+  else if constexpr (AUX == 0)
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+  else
+    asm volatile("buffer_load_dword %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc),
+                 "{m0}"(lds_base)
+                 : "memory");
+}
+
+// Raw buffer descriptor words over `bytes` bytes from `base` (wave-uniform):
+// base address, stride 0, record count, dword data format (as CDNA expects).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;
+  return r;
+}
+
+// Copy rows 0 .. kChunk - 1 (from `rows`, the tile's first element in the
+// chunk's first step) of one input tensor's channel tile straight from global
+// memory into LDS (no registers involved). Each copy instruction gets its own
+// buffer descriptor, built in scalar registers, that starts at its first row
+// and ends at the segment's end (`rows_left` rows from `rows`): rows past the
+// segment read as zero, as do pieces past the last channel (`lane_off`); they
+// are never used. Lane i of wave `wv` lands S * i bytes after the wave's LDS
+// base. The caller waits for the copies (wait_vmem) and synchronises the
+// workgroup before the tile is read (see lds_copy).
 template <class IO, int S, int AUX = 0, int KC = kChunk>
 __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t rows_left,
                                          uint32_t row_bytes, typename IO::raw* tile, int wv,
@@ -74,22 +124,18 @@ __device__ __forceinline__ void dma_tile(const typename IO::raw* rows, uint32_t 
   constexpr int kPerInstr = kBlock * S;
   constexpr int kRowsPerInstr = S / eb;
   static_assert(kTileBytes % kPerInstr == 0, "tile must be a whole number of copies");
-  static_assert(S == 16 || S == 4, "copies are 16 or 4 bytes per lane");
 #pragma unroll
   for (int k = 0; k < kTileBytes / kPerInstr; ++k) {
     const uint32_t r0 = k * kRowsPerInstr;
-    // wave-uniform; read into a scalar register so the resource is built there
     const uint32_t left = uniform_u32(rows_left > r0 ? rows_left - r0 : 0u);
-    const auto r = make_rsrc(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
+    const u32x4 r = rsrc_words(reinterpret_cast<const char*>(rows) + r0 * row_bytes, left * row_bytes);
     char* dst = reinterpret_cast<char*>(tile) + (k * kBlock + wv * 64) * S;
-    if constexpr (S == 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, lane_off, 0, 0, AUX);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 4, lane_off, 0, 0, AUX);
+    const uint32_t lds_base = uniform_u32(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(dst))));
+    lds_copy<S, AUX>(r, lane_off, lds_base);
   }
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Write the y tile of one chunk from LDS to HBM in the pieces of dma_tile
 // (same per-instruction resources, so rows past the segment are dropped;
