@@ -7,19 +7,29 @@ fp32 state, with bias, softplus, D skip and silu(z) gate. Inputs are seeded
 synthetic tensors already resident in HBM; the timed region holds exactly
 --steps calls bracketed by device synchronisation.
 
+Two input sets are alternated between calls, so consecutive calls do not
+find their inputs in the caches.
+
 Prints one JSON line. `value` is elem-steps/s (batch * L * channels per
 second). `roofline` relates the scan call's algorithmic fp32 operations to
-the vector-ALU peak (the scan is bound by vector-ALU issue), from its average
-launch time measured with HIP events on the launch stream; `hbm` gives the
+the published fp32 vector-ALU peak (the scan is bound by vector-ALU issue),
+from its average launch time measured with HIP events on the launch stream,
+with `traffic` the HBM bytes per call that rocprofv3 measured for the same
+kernel sources (profiles/, null once the sources change); `hbm` gives the
 same call's algorithmic HBM bytes (every input read once, y and the final
-state written once) against the HBM peak. `cpu_baseline` is the fp64 oracle
-timed on this host on a bounded sample of the same workload. Measured in the
-same run, each with its own roofline: the backward call on the same layer
+state written once) against the HBM peak; `flushed` times the call with
+512 MB written between calls (more than the 256 MB last-level cache).
+`cpu_baseline` is the fp64 oracle timed on this host on every core of the
+process's affinity set over the whole workload (plus one thread on a sample).
+Measured in the same run, each with its own roofline: the scan on the
+130M-shaped layer (`fwd_130m`) and on 131,072 tokens (`fwd_131k`), both with
+flushed caches and alternated inputs; the backward call on the 2.8B layer
 (`bwd`), the decode step (64 one-token updates of a 4,096 x 5,120 x 16 fp32
 state, `decode`), the causal convolution front-end (`conv`) and the Mamba-2
 SSD layer (80 heads of 64, N = 128, 8 x 2048, `ssd`, against the bf16
 matrix-core peak), and the same forward scan through the opt-in state-split
-kernel (`fwd_split`), for comparison with the default kernel.
+kernel (`fwd_split`), for comparison with the default kernel. `--parts`
+selects a subset (profiling runs use one part each).
 """
 from __future__ import annotations
 
