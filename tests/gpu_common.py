@@ -31,17 +31,18 @@ def norm_err(got, ref) -> float:
     return float(np.max(np.abs(got - ref) / denom))
 
 
-def plain_rel_err(got, ref) -> float:
+def plain_rel_err(got, ref, floor=1.0) -> float:
     """Plain elementwise relative error max |g - r| / |r| over the entries with
-    |r| >= rms(r) (reported beside norm_err: on those entries the two differ by
-    at most a factor of 2; below rms(r) a plain relative error measures the
-    cancellation in a sum of 16 products, not the kernel)."""
+    |r| >= floor * rms(r) (reported beside norm_err: with floor = 1 the two
+    differ by at most a factor of 2 on those entries; far below rms(r) a plain
+    relative error measures the cancellation in a sum of 16 products, not the
+    kernel)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if ref.size == 0:
         return 0.0
     rms = float(np.sqrt(np.mean(ref * ref)))
-    big = np.abs(ref) >= rms
+    big = np.abs(ref) >= floor * rms
     if rms == 0.0 or not np.any(big):
         return 0.0
     return float(np.max(np.abs(got[big] - ref[big]) / np.abs(ref[big])))

@@ -62,11 +62,15 @@ def _compare(label, io, y, h, ry, rh):
     tol = TOL[io]
     ey, eh = norm_err(_f(y), ry), norm_err(_f(h), rh)
     py, ph = plain_rel_err(_f(y), ry), plain_rel_err(_f(h), rh)
+    py3 = plain_rel_err(_f(y), ry, floor=1e-3)
     _say(f"{label}: err(y)={ey:.3e} err(state)={eh:.3e} plain rel (|r|>=rms) y={py:.3e} "
-         f"state={ph:.3e} tol={tol:g}")
+         f"state={ph:.3e} (|r|>=1e-3 rms) y={py3:.3e} tol={tol:g}")
     assert np.all(np.isfinite(_f(y))) and np.all(np.isfinite(_f(h)))
     assert ey <= tol, f"y error {ey} > {tol}"
     assert eh <= tol, f"state error {eh} > {tol}"
+    if io == "f32":
+        assert py <= tol, f"plain y error {py} > {tol}"
+        assert ph <= tol, f"plain state error {ph} > {tol}"
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import TOL, BlockedErr, gpu_decode, gpu_scan, norm_err, oracle_scan, to_dev
+from gpu_common import plain_rel_err, TOL, BlockedErr, gpu_decode, gpu_scan, norm_err, oracle_scan, to_dev
 from selective_state_space_56_amd import scan_fwd, state_update
 from selective_state_space_56_amd.workloads import (WORKLOADS, make_decode_state, make_decode_token,
                                                     make_params, make_scan_inputs, make_trained_A,
@@ -35,10 +35,18 @@ def _check_scan(orc, w, inp, segments=0, channels=None, tol=None, **kw):
         got_y = got_y[:, :, channels]
         got_h = got_h[:, channels]
     ey, eh = norm_err(got_y, ref_y), norm_err(got_h, ref_h)
+    py, ph = plain_rel_err(got_y, ref_y), plain_rel_err(got_h, ref_h)
+    py3 = plain_rel_err(got_y, ref_y, floor=1e-3)
     _say(f"{w.name} {w.batch}x{w.seqlen}x{w.dim} N={w.dstate} seg={segments}: "
-         f"err(y)={ey:.3e} err(state)={eh:.3e} tol={tol:g}")
+         f"err(y)={ey:.3e} err(state)={eh:.3e} tol={tol:g}; plain rel |r|>=rms y={py:.3e} "
+         f"state={ph:.3e}, |r|>=1e-3 rms y={py3:.3e}")
     assert ey <= tol, f"y error {ey} > {tol}"
     assert eh <= tol, f"state error {eh} > {tol}"
+    if w.io == "f32":
+        # fp32: the plain relative error itself meets the tolerance wherever
+        # |r| is at least rms(r)
+        assert py <= tol, f"plain y error {py} > {tol}"
+        assert ph <= tol, f"plain state error {ph} > {tol}"
     return ey, eh
 
 
