@@ -1000,11 +1000,14 @@ ScanBwdPlan plan_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate
   const int64_t rows = batch * dim;
   int segs = forced_segments;
   if (segs <= 0 && rows > 0 && seqlen > 0) {
-    // Cut the sequence into enough segments for about two rounds of the main
-    // pass's resident workgroups, each at least 48 steps long.
+    // Cut the sequence into enough segments for about four rounds of the main
+    // pass's resident workgroups, each at least 48 steps long. (On the
+    // 8 x 2048 x 5120 layer: 12 segments, 1.49 ms per call against 1.55 ms with
+    // two rounds; with two workgroups per compute unit the last, partly filled
+    // round costs less when the rounds are short.)
     const int64_t blocks = batch * ((dim + kBlock - 1) / kBlock);
     const int64_t slots = static_cast<int64_t>(device_cu_count()) * kMainBlocksPerCU<Bf16Io>;
-    int64_t v = 2 * slots / blocks;
+    int64_t v = 4 * slots / blocks;
     if (v > seqlen / 48) v = seqlen / 48;
     segs = static_cast<int>(v < 1 ? 1 : (v > 4096 ? 4096 : v));
   }
