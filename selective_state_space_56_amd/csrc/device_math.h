@@ -106,11 +106,15 @@ struct Bf16Io {
 // the result by at most |r| (1 - 1/w) <= 2^-24 e, below 2^-23 of the result
 // (log(1 + e) >= e ln 2 on (0, 1]). e never overflows, so large u needs no
 // special case: the log term vanishes and max(u, 0) = u remains.
-__device__ __forceinline__ float softplus_f(float u) {
-  const float e = hw_exp2(-fabsf(u) * kLog2e);
+// max(u, 0) is formed as (u + |u|) / 2 (exact: 2u or 0, halved), one add with
+// an operand modifier and the final fma, instead of a max (which gfx950
+// issues at half the rate of adds and fmas). neg_log2e is -log2(e); a caller
+// in a hot loop may pass it from a vector register, for the same reason.
+__device__ __forceinline__ float softplus_f(float u, float neg_log2e = -kLog2e) {
+  const float e = hw_exp2(fabsf(u) * neg_log2e);
   const float w = 1.0f + e;
   const float r = e - (w - 1.0f);
-  return fmaxf(u, 0.0f) + fmaf(hw_log2(w), kLn2, r);
+  return fmaf(0.5f, u + fabsf(u), fmaf(hw_log2(w), kLn2, r));
 }
 
 // silu(v) = v * sigmoid(v) = v / (1 + e^-v). For v -> -inf, e^-v = inf and the

@@ -75,10 +75,11 @@ struct FrontEnd {
 
 template <int N, class IO, int MODE, bool GATE, bool STRUCTURED>
 __device__ __forceinline__ FrontEnd front_end(typename IO::raw xr, typename IO::raw dr,
-                                              typename IO::raw zr, float a2_0, float bias) {
+                                              typename IO::raw zr, float a2_0, float bias,
+                                              float neg_log2e) {
   FrontEnd f;
   f.xf = IO::to_f32(xr);
-  f.Delta = softplus_f(IO::to_f32(dr) + bias);
+  f.Delta = softplus_f(IO::to_f32(dr) + bias, neg_log2e);
   if (STRUCTURED) {
     f.dx = fmaf(f.Delta, f.xf, copysignf(kDxFloor, f.xf));
     f.rdx = hw_rcp(f.dx);
@@ -256,6 +257,11 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const float Dd = (MODE == kOutput && D) ? D[d] : 0.0f;
   const float bias = bias_p ? bias_p[d] : 0.0f;
 
+  // -log2(e) held in a vector register: the softplus multiply then takes two
+  // vector operands, a form gfx950 issues at the full rate (a scalar-register
+  // operand halves it)
+  float neg_log2e = -kLog2e;
+  asm volatile("" : "+v"(neg_log2e));
   float h[N];
   if (MODE == kOutput && (s > 0 || g.h0 != nullptr)) {
     // carry-in: the folded state after segment s - 1, or the initial state
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       const int valid = FULL ? kChunk : static_cast<int>(steps - t0);
       FrontEnd fe = front_end<N, IO, MODE, GATE, KSTRUCT>(
           st.in[buf][0][0][tid], st.in[buf][1][0][tid], kZ ? st.in[buf][kZi][0][tid] : raw(0), A2[0],
-          bias);
+          bias, neg_log2e);
       float dsum = 0.0f;  // this chunk's Delta (aggregate mode)
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           if (j + 1 < kChunk && (FULL || j + 1 < valid))
             fn = front_end<N, IO, MODE, GATE, KSTRUCT>(
                 st.in[buf][0][js + 1][tid], st.in[buf][1][js + 1][tid],
-                kZ ? st.in[buf][kZi][js + 1][tid] : raw(0), A2[0], bias);
+                kZ ? st.in[buf][kZi][js + 1][tid] : raw(0), A2[0], bias, neg_log2e);
           float bc[2 * N];
           read_bc<N>(st.bc[buf][js], bc, kC);
           const raw y =

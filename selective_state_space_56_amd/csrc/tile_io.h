@@ -16,18 +16,17 @@ static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
 constexpr int kAuxBlock = 256;       // threads per workgroup of the small helper kernels
 constexpr int kChunk = 8;     // time steps whose inputs are loaded together
 
-// p[n] = rho e^(n+1) for n = 0..N-1: rho e, then blocks doubling in length,
-// block b (n = b .. 2b-1) being block 0 .. b-1 times e^b (N + log2 N - 1
-// multiplications, at most 1 + log2 N deep).
+// p[n] = rho e^(n+1) for n = 0..N-1 as two interleaved chains: rho e and
+// rho e^2, then p[n] = p[n - 2] e^2 (N + 1 multiplications, at most N / 2 + 1
+// deep; the states' own updates interleave with the two chains).
 template <int N>
 __device__ __forceinline__ void scaled_powers(float e, float rho, float (&p)[N]) {
   p[0] = rho * e;
-  float eb = e;
+  if constexpr (N > 1) {
+    p[1] = p[0] * e;
+    const float e2 = e * e;
 #pragma unroll
-  for (int b = 1; b < N; b *= 2) {
-    if (b > 1) eb = eb * eb;
-#pragma unroll
-    for (int i = 0; i < b; ++i) p[b + i] = p[i] * eb;
+    for (int n = 2; n < N; ++n) p[n] = p[n - 2] * e2;
   }
 }
 
