@@ -11,15 +11,14 @@
 // When there are too few rows to fill the GPU, the sequence is cut into time
 // segments that run in parallel and are stitched with the associative
 // affine-pair combine (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2) (same page,
-// same section), in three launches:
+// same section), in two launches:
 //   1. aggregate: each segment but the last scans from h = 0 and records its
 //      end state and the sum of its Delta (the segment's decay for state n is
 //      exp(A_n * sum Delta), a product of per-step decays);
-//   2. combine: a sequential fold over segments per (row, n), from the initial
-//      state (zero, or the caller's h0), turns the
-//      aggregates into each segment's carry-in state;
-//   3. output: every segment re-scans from its carry-in and writes y (and the
-//      last one the final state).
+//   2. output: every segment folds the aggregates of the segments before it
+//      onto the initial state (zero, or the caller's h0) in time order, which
+//      gives its carry-in, re-scans from there and writes y (and the last one
+//      the final state).
 #include <atomic>
 #include <type_traits>
 
@@ -44,6 +43,7 @@ struct Dims {
   int64_t group_dim;     // channels per group (a multiple of kBlock when ngroups > 1)
   // elements between consecutive steps: x, Delta_raw, z, out, and B / C
   int64_t sx, sd, sz, so, sbc;
+  bool carries_folded;   // the fold launch has turned the aggregates into carry-ins
 };
 
 enum Mode { kOutput = 0, kAggregate = 1 };
@@ -169,6 +169,15 @@ struct __align__(16) Stage {
 // exact zero-order-hold input weight, for every tile.
 enum PathSet { kPathGeneral = 0, kPathStructured = 1, kPathBoth = 2, kPathGeneralZoh = 3 };
 
+// Up to this many segments the output pass folds the segment aggregates into
+// its carry-in itself (at most kFoldInOutputMax - 1 folds per lane); beyond,
+// the fold launch does it once per (row, state) and the output pass reads the
+// result. On the 8 x 2048 x 5120 layer (12 segments) folding in the output
+// pass saves the 12.6 us fold launch (328 -> 318 us per call); with 42
+// segments of 48 steps (2 x 2048 x 1536) or 102 of 1,285 (131,072 tokens) the
+// per-lane folds cost more than the launch.
+constexpr int kFoldInOutputMax = 16;
+
 // Both decay paths in one kernel per pass (a per-workgroup branch): on the
 // 8 x 2048 x 5120 layer the kernels took the same time as with one launch per
 // path (bitwise the same results), and two launches per call are saved.
@@ -263,15 +272,30 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   float neg_log2e = -kLog2e;
   asm volatile("" : "+v"(neg_log2e));
   float h[N];
-  if (MODE == kOutput && (s > 0 || g.h0 != nullptr)) {
-    // carry-in: the folded state after segment s - 1, or the initial state
-    const float* hin = s > 0 ? ws_h + (static_cast<int64_t>(s - 1) * g.rows + row) * N
-                             : g.h0 + row * N;
+  if (MODE == kOutput && g.h0 != nullptr) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = hin[n];
+    for (int n = 0; n < N; ++n) h[n] = g.h0[row * N + n];
   } else {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  }
+  if (MODE == kOutput && g.carries_folded && s > 0) {
+    // carry-in from the fold launch: slot s - 1
+    const float* hin = ws_h + (static_cast<int64_t>(s - 1) * g.rows + row) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = hin[n];
+  } else if (MODE == kOutput) {
+    // carry-in: the aggregates of segments 0 .. s - 1 (end state from zero,
+    // sum of Delta) folded onto the initial state in time order, each by the
+    // pair combine h <- exp(A sum Delta) h + end state, the arithmetic of the
+    // fold launch (same results). With few segments (kFoldInOutputMax) this
+    // costs less than a launch of its own.
+    for (int k = 0; k < s; ++k) {
+      const float sk = ws_s[static_cast<int64_t>(k) * g.rows + row];
+      const float* agg = ws_h + (static_cast<int64_t>(k) * g.rows + row) * N;
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = fmaf(hw_exp2(A2[n] * sk), h[n], agg[n]);
+    }
   }
 
   // buffer resources at (b, t_begin, first channel of the tile), per tensor
@@ -462,7 +486,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
 // state from zero, sum of Delta) on entry and the carry-in state of segment
 // k + 1 on exit. The slots are read in blocks of
 // kFoldBlock before they are folded and written, so the loads of a block are
-// in flight together.
+// in flight together. (The forward scan folds inside its output pass; the
+// backward's state checkpoints use this kernel.)
 constexpr int kFoldBlock = 8;
 
 template <int N>
@@ -505,6 +530,15 @@ __global__ __launch_bounds__(kAuxBlock) void init_state_kernel(float* dst, const
   if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
+template <int N>
+void launch_fold(const ScanProblem& p, const Dims& g, float* ws_h, const float* ws_s,
+                 hipStream_t stream) {
+  const int64_t work = g.rows * N;
+  hipLaunchKernelGGL((scan_combine_kernel<N>),
+                     dim3(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock)), dim3(kAuxBlock),
+                     0, stream, p.A, ws_h, ws_s, p.h0, g.rows, p.dim, g.segments);
+}
+
 template <int N, class IO, int CW>
 hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* workspace,
                         hipStream_t stream) {
@@ -524,6 +558,7 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
   g.sz = p.z ? p.sz : p.sx;
   g.so = p.so;
   g.sbc = p.sbc;
+  g.carries_folded = plan.segments > kFoldInOutputMax;
   // The workspace (segment aggregates, then the tile flags) exists only with
   // more than one segment; a single-segment plan ignores any buffer passed
   // in, so no kernel reads flags that this call did not write.
@@ -547,11 +582,7 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
       hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, kPathGeneralZoh>),
                          dim3(blocks, plan.segments - 1), block, 0, stream, x, dl, p.A, B, C, p.D,
                          z, p.bias, out, p.last_state, ws_h, ws_s, g);
-      const int64_t work = g.rows * N;
-      hipLaunchKernelGGL((scan_combine_kernel<N>),
-                         dim3(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock)),
-                         dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s, p.h0, g.rows, p.dim,
-                         plan.segments);
+      if (g.carries_folded) launch_fold<N>(p, g, ws_h, ws_s, stream);
     }
     const dim3 grid(blocks, plan.segments);
     if (z)
@@ -576,10 +607,7 @@ hipError_t launch_typed(const ScanProblem& p, const ScanPlan& plan, void* worksp
       hipLaunchKernelGGL((scan_segment_kernel<N, IO, kAggregate, false, CW, kPathGeneral>),
                          grid_agg, block, 0, stream, x, dl, p.A, B, C, p.D, z, p.bias, out,
                          p.last_state, ws_h, ws_s, g);
-    const int64_t work = g.rows * N;
-    const dim3 grid_c(static_cast<unsigned>((work + kAuxBlock - 1) / kAuxBlock));
-    hipLaunchKernelGGL((scan_combine_kernel<N>), grid_c, dim3(kAuxBlock), 0, stream, p.A, ws_h, ws_s,
-                       p.h0, g.rows, p.dim, plan.segments);
+    if (g.carries_folded) launch_fold<N>(p, g, ws_h, ws_s, stream);
   }
   const dim3 grid(blocks, plan.segments);
   if (z) {
@@ -657,8 +685,8 @@ int device_cu_count() { return device_cus(); }
 // the segment aggregates (end states, Delta sums) and tile flags of one call,
 // in a file-scope device array, one copy per GPU the library runs on, held
 // until the process ends. Every word a call reads from it is written earlier
-// in the same call (aggregate launch, then fold, then output launch, all on
-// the caller's stream), so nothing needs clearing between calls; calls that
+// in the same call (aggregate launch, then output launch, both on the
+// caller's stream), so nothing needs clearing between calls; calls that
 // overlap in time on one GPU race on it. The library's own segment plan needs
 // at most about 36 MB on a 256-CU device (two rounds of output workgroups of
 // 256 channels, 68 bytes per channel and segment).
