@@ -60,6 +60,24 @@ __device__ __forceinline__ float from_bf16(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two values rounded to bf16 (nearest even) in one register, a in the low
+// half: one v_cvt_pk_bf16_f32 for both.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+// a and b each as a bf16 pair hi + lo (hi = bf16(v), lo = bf16(v - hi)),
+// packed two values per register like pack_bf16; the same roundings as
+// to_bf16 element by element, with half the conversions.
+struct Bf16Pairs {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Bf16Pairs split_bf16_pair(float a, float b) {
+  const uint32_t hi = pack_bf16(a, b);
+  return {hi, pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u))};
+}
+
 // Eight bf16 at p (16-byte aligned), as an MFMA operand.
 __device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
@@ -229,15 +247,16 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunk_state_kernel(
         const float w = t < g.seqlen
                             ? hw_exp2((ell_last - s_ell[k * kSBlk + row]) * kLog2e) * s_delta[k * kSBlk + row]
                             : 0.0f;
-        u16x8 vh, vl;
+        u32x4 vh, vl;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = from_bf16(xv[q][e]) * w;
-          vh[e] = to_bf16(v);
-          vl[e] = to_bf16(v - from_bf16(vh[e]));
+        for (int e = 0; e < 4; ++e)
+        {
+          const Bf16Pairs hl = split_bf16_pair(from_bf16(xv[q][2 * e]) * w, from_bf16(xv[q][2 * e + 1]) * w);
+          vh[e] = hl.hi;
+          vl[e] = hl.lo;
         }
-        *reinterpret_cast<u16x8*>(&s_xh[row][8 * (id & 7)]) = vh;
-        *reinterpret_cast<u16x8*>(&s_xl[row][8 * (id & 7)]) = vl;
+        *reinterpret_cast<u32x4*>(&s_xh[row][8 * (id & 7)]) = vh;
+        *reinterpret_cast<u32x4*>(&s_xl[row][8 * (id & 7)]) = vl;
       }
 #pragma unroll
       for (int q = 0; q < kBP; ++q) {
@@ -390,16 +409,17 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
   // S_in as a bf16 pair hi + lo (hi + lo = S_in to about 2^-17 relative)
 #pragma unroll
   for (int k = 0; k < kSPieces; ++k) {
-    typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int id = tid + kScanThreads * k;
-    u16x4 vh, vl;
+    u32x2 vh, vl;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vh[e] = to_bf16(sv[k][e]);
-      vl[e] = to_bf16(sv[k][e] - from_bf16(vh[e]));
+    for (int e = 0; e < 2; ++e) {
+      const Bf16Pairs hl = split_bf16_pair(sv[k][2 * e], sv[k][2 * e + 1]);
+      vh[e] = hl.hi;
+      vl[e] = hl.lo;
     }
-    *reinterpret_cast<u16x4*>(&s_sh[id >> 5][4 * (id & 31)]) = vh;
-    *reinterpret_cast<u16x4*>(&s_sl[id >> 5][4 * (id & 31)]) = vl;
+    *reinterpret_cast<u32x2*>(&s_sh[id >> 5][4 * (id & 31)]) = vh;
+    *reinterpret_cast<u32x2*>(&s_sl[id >> 5][4 * (id & 31)]) = vl;
   }
   __syncthreads();
   const float Dh = D ? D[h] : 0.0f;
@@ -477,11 +497,12 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
       // hundreds of such terms into one output
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        u16x8 pk, pl;
+        u32x4 pk, pl;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pk[k] = to_bf16(e[8 * q + k]);
-          pl[k] = to_bf16(e[8 * q + k] - from_bf16(pk[k]));
+        for (int k = 0; k < 4; ++k) {
+          const Bf16Pairs hl = split_bf16_pair(e[8 * q + 2 * k], e[8 * q + 2 * k + 1]);
+          pk[k] = hl.hi;
+          pl[k] = hl.lo;
         }
         const bf16x8 aop = __builtin_bit_cast(bf16x8, pk);
         const bf16x8 alo = __builtin_bit_cast(bf16x8, pl);
