@@ -18,7 +18,8 @@
 //   2. output: every segment folds the aggregates of the segments before it
 //      onto the initial state (zero, or the caller's h0) in time order, which
 //      gives its carry-in, re-scans from there and writes y (and the last one
-//      the final state).
+//      the final state). With many segments a fold launch between the two
+//      does the folds once per (row, state) instead (kFoldInOutputMax).
 #include <atomic>
 #include <type_traits>
 
