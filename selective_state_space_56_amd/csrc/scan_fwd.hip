@@ -290,12 +290,26 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     // sum of Delta) folded onto the initial state in time order, each by the
     // pair combine h <- exp(A sum Delta) h + end state, the arithmetic of the
     // fold launch (same results). With few segments (kFoldInOutputMax) this
-    // costs less than a launch of its own.
-    for (int k = 0; k < s; ++k) {
-      const float sk = ws_s[static_cast<int64_t>(k) * g.rows + row];
-      const float* agg = ws_h + (static_cast<int64_t>(k) * g.rows + row) * N;
+    // costs less than a launch of its own. The aggregates are read four at a
+    // time, so their loads are in flight together.
+    constexpr int kFb = 4;
+    for (int k0 = 0; k0 < s; k0 += kFb) {
+      float sv[kFb], av[kFb][N];
 #pragma unroll
-      for (int n = 0; n < N; ++n) h[n] = fmaf(hw_exp2(A2[n] * sk), h[n], agg[n]);
+      for (int u = 0; u < kFb; ++u) {
+        const int k = k0 + u < s ? k0 + u : s - 1;  // past s: a valid slot, unused
+        sv[u] = ws_s[static_cast<int64_t>(k) * g.rows + row];
+        const float* agg = ws_h + (static_cast<int64_t>(k) * g.rows + row) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) av[u][n] = agg[n];
+      }
+#pragma unroll
+      for (int u = 0; u < kFb; ++u) {
+        if (k0 + u < s) {
+#pragma unroll
+          for (int n = 0; n < N; ++n) h[n] = fmaf(hw_exp2(A2[n] * sv[u]), h[n], av[u][n]);
+        }
+      }
     }
   }
 
