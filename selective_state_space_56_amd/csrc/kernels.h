@@ -33,8 +33,9 @@ struct ScanProblem {
 };
 
 // Time segmentation of a full-sequence scan: the sequence is cut into
-// `segments` pieces of `seg_len` steps (the last may be shorter) that are
-// scanned in parallel and stitched by the affine-pair combine.
+// `segments` pieces of `seg_len` steps (the last takes the rest: shorter, or
+// longer in plans that lengthen it) that are scanned in parallel and stitched
+// by the affine-pair combine.
 struct ScanPlan {
   int64_t seg_len;
   int segments;

@@ -279,6 +279,17 @@ def test_prefill_2p8b_general_A_full_size(orc, dev):
     _check_full_blocked(orc, w, inp, 1024, w.name + " general A")
 
 
+def test_long_last_segment_plan(orc, dev):
+    """8 x 581 x 5120 bf16 with the library's own plan, which on a 256-CU
+    device cuts ten segments of 40 steps and a last one of 181 (the output
+    pass starts that long last segment first; 581 steps end in a partial
+    chunk), every output compared."""
+    w = WORKLOADS["mamba2p8b_prefill"].with_shape(name="long_last", seqlen=581)
+    _say(f"case {w.name} (library plan, every channel)")
+    inp = make_scan_inputs(w, seed=581, device=dev)
+    _check_full_blocked(orc, w, inp, 1024, w.name)
+
+
 def test_long_context_full_size(orc, dev):
     """131,072 tokens at 5,120 channels in one call (102 segments by the
     library's plan), every output compared."""

@@ -39,6 +39,7 @@ def _f(t):
     ("mamba130m_layer", 2, 600, 320, "bf16", 0, False, False),
     ("mamba130m_layer", 2, 600, 320, "bf16", 4, True, True),
     ("mamba130m_layer", 1, 100, 37, "bf16", 1, True, False),   # register-staged tiles
+    ("mamba2p8b_prefill", 8, 581, 5120, "bf16", 0, True, True),  # long last segment
 ])
 def test_zoh_scan_vs_oracle(orc, dev, name, batch, L, dim, io, segments, trained, with_h0):
     w = WORKLOADS[name].with_shape(name="zoh", batch=batch, seqlen=L, dim=dim, io=io)
