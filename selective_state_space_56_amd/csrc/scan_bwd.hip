@@ -201,6 +201,7 @@ struct __align__(16) BwdStage {
   typename IO::raw go[NOUT ? 2 : 1][NOUT ? NOUT : 1][NOUT ? kChunk : 1][kBlock];
   float red[NOUT ? kBlock / 64 : 1][NOUT ? kChunk : 1][2 * N];
   float dl[NOUT ? kChunk : 1][kBlock];  // Delta of the chunk's steps, per lane
+  float dxs[NOUT ? kChunk : 1][kBlock];  // their floored Delta x (structured tiles)
 };
 
 // Addressing of one workgroup's channel tile within one time segment, shared
@@ -327,6 +328,31 @@ struct Decays {
     } else {
       return hw_exp2(Delta * A2[n]);
     }
+  }
+};
+
+// rho e^(n+1) for n = 0, 1, ... in turn, as two interleaved chains (rho e and
+// rho e^2, then each value times e^2): the same products as scaled_powers with
+// two values live instead of N.
+template <int N>
+struct PowerChains {
+  float even, odd, e2;
+  __device__ __forceinline__ PowerChains(float e, float rho) {
+    even = rho * e;
+    odd = even * e;
+    e2 = e * e;
+  }
+  // call for n = 0, 1, ... in turn
+  __device__ __forceinline__ float next(int n) {
+    float v;
+    if (n & 1) {
+      v = odd;
+      odd *= e2;
+    } else {
+      v = even;
+      even *= e2;
+    }
+    return v;
   }
 };
 
@@ -668,7 +694,12 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
 
   // Reverse sweep over the chunks.
   float m[N];  // abar_{t+1} lam_{t+1}: the adjoint entering from later time
-  if (s + 1 < g.segments) {
+  // (zeros on lanes past the last channel, so that every term they add to the
+  // channel sums of dB and dC is zero in both forms of the step below)
+  if (!active) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) m[n] = 0.0f;
+  } else if (s + 1 < g.segments) {
     const float* ain = a.carry_a + (static_cast<int64_t>(s) * g.rows + tc.row) * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) m[n] = ain[n];
@@ -701,8 +732,12 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
       tc.fetch_bc((c - 1) * kChunk, bcv);
     }
     const int valid = static_cast<int>(tc.steps) - c * kChunk;
-    // recompute the chunk's states h_t (from the checkpoint before its first
-    // step; zeros on lanes past the last channel)
+    // recompute the chunk's states (from the checkpoint before its first
+    // step; zeros on lanes past the last channel): h_t, or on S4D-Real-shaped
+    // tiles g_t = h_t / dx_t with dx_t = Delta_t x_t kept away from zero by at
+    // most 1e-20 (the forward scan's rescaled form: g_t = rho_t e^(n+1) g_{t-1}
+    // + B_t with rho_t = dx_{t-1} / dx_t, and at the chunk's first step
+    // g = e^(n+1) h / dx + B from the state h before it)
     float hist[kChunk][N];
     {
       float hc[N];
@@ -719,19 +754,38 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
 #pragma unroll
         for (int n = 0; n < N; ++n) hc[n] = fmaf(dk.next(n, A2), cin[n], hc[n]);
       }
+      float dx_prev = 1.0f;
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         if (j < valid) {
           const float Delta = softplus_f(u_at(buf, j));
           st.dl[j][tid] = Delta;
-          const float dxv = Delta * x_at(buf, j);
+          const float xf = x_at(buf, j);
           const float* Br = &st.bc[buf][j][0];
-          Decays<N, STRUCT> ab(Delta, A2);
+          if constexpr (STRUCT) {
+            const float dx = fmaf(Delta, xf, copysignf(kDxFloorBwd, xf));
+            st.dxs[j][tid] = dx;
+            const float rdx = hw_rcp(dx);
+            PowerChains<N> pw(hw_exp2(Delta * A2[0]), j == 0 ? rdx : dx_prev * rdx);
+            dx_prev = dx;
 #pragma unroll
-          for (int n = 0; n < N; ++n)
-            hist[j][n] = fmaf(ab.next(n, A2), j == 0 ? hc[n] : hist[j - 1][n], dxv * Br[n]);
+            for (int n = 0; n < N; ++n)
+              hist[j][n] = fmaf(pw.next(n), j == 0 ? hc[n] : hist[j - 1][n], Br[n]);
+          } else {
+            const float dxv = Delta * xf;
+            Decays<N, STRUCT> ab(Delta, A2);
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+              hist[j][n] = fmaf(ab.next(n, A2), j == 0 ? hc[n] : hist[j - 1][n], dxv * Br[n]);
+          }
         }
       }
+    }
+    if constexpr (STRUCT) {
+      // the adjoint enters the chunk's last step scaled like it: m dx there
+      const float dx_top = st.dxs[valid < kChunk ? valid - 1 : kChunk - 1][tid];
+#pragma unroll
+      for (int n = 0; n < N; ++n) m[n] *= dx_top;
     }
     // step the adjoint back through them
 #pragma unroll
@@ -749,25 +803,58 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
           ds = dyv * (zf * sz);
         }
         ds = active ? ds : 0.0f;
-        const float dxv = Delta * xf;
         float bc[2 * N];
         read_bc<N>(st.bc[buf][j], bc, true);
-        Decays<N, STRUCT> ab(Delta, A2);
         float sAq = 0.0f, sLB = 0.0f, ypre = Dd * xf;
         float r[N];  // dB / dC terms of this step after the first halving level
+        if constexpr (STRUCT) {
+          // Scaled adjoint l_t = lam_t dx_t: l_t = C_t ds_t dx_t + mu_{t+1},
+          // mu_t = alpha_t l_t with the forward's alpha_t = rho_t e^(n+1)
+          // (m holds mu_{t+1}). Then the dB term Delta_t x_t lam_t is
+          // l_t Delta_t x_t / dx_t, ds_t h_t = ds_t dx_t g_t, and
+          // abar_t lam_t h_{t-1} = mu_t g_{t-1}, or l_t (g_t - B_t) at the
+          // chunk's first step, whose mu_t (rho = 1 / dx) is the unscaled
+          // abar_t lam_t that enters the previous chunk.
+          const float dx = st.dxs[j][tid];
+          const float rdx = hw_rcp(dx);
+          const float dsdx = ds * dx;
+          const float kappa = Delta * xf * rdx;  // Delta x / dx: 1 but for the floor
+          PowerChains<N> pw(hw_exp2(Delta * A2[0]),
+                            j == 0 ? rdx : st.dxs[j > 0 ? j - 1 : 0][tid] * rdx);
+          float sLBs = 0.0f, ypg = 0.0f;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-          const float lam = fmaf(bc[N + n], ds, m[n]);
-          // abar_t h_{t-1} = h_t - Delta_t B_t x_t
-          const float q = lam * fmaf(-dxv, bc[n], hist[j][n]);
-          dA[n] = fmaf(Delta, q, dA[n]);
-          sAq = fmaf(STRUCT ? static_cast<float>(n + 1) : A2[n], q, sAq);
-          sLB = fmaf(lam, bc[n], sLB);
-          ypre = fmaf(bc[N + n], hist[j][n], ypre);
-          r[n] = BcReduce<N>::level0(lam * dxv, ds * hist[j][n]);
-          m[n] = ab.next(n, A2) * lam;
+          for (int n = 0; n < N; ++n) {
+            // (mu last, so that it can take l's register, which is m's)
+            const float l = fmaf(bc[N + n], dsdx, m[n]);
+            sLBs = fmaf(l, bc[n], sLBs);
+            ypg = fmaf(bc[N + n], hist[j][n], ypg);
+            r[n] = BcReduce<N>::level0(l * kappa, dsdx * hist[j][n]);
+            float q;
+            if (j == 0) q = l * (hist[0][n] - bc[n]);
+            m[n] = pw.next(n) * l;
+            if (j != 0) q = m[n] * hist[j > 0 ? j - 1 : 0][n];
+            dA[n] = fmaf(Delta, q, dA[n]);
+            sAq = fmaf(static_cast<float>(n + 1), q, sAq);
+          }
+          sAq *= A2[0];
+          sLB = sLBs * rdx;
+          ypre = fmaf(dx, ypg, ypre);
+        } else {
+          const float dxv = Delta * xf;
+          Decays<N, STRUCT> ab(Delta, A2);
+#pragma unroll
+          for (int n = 0; n < N; ++n) {
+            const float lam = fmaf(bc[N + n], ds, m[n]);
+            // abar_t h_{t-1} = h_t - Delta_t B_t x_t
+            const float q = lam * fmaf(-dxv, bc[n], hist[j][n]);
+            dA[n] = fmaf(Delta, q, dA[n]);
+            sAq = fmaf(A2[n], q, sAq);
+            sLB = fmaf(lam, bc[n], sLB);
+            ypre = fmaf(bc[N + n], hist[j][n], ypre);
+            r[n] = BcReduce<N>::level0(lam * dxv, ds * hist[j][n]);
+            m[n] = ab.next(n, A2) * lam;
+          }
         }
-        if (STRUCT) sAq *= A2[0];
         const float tot = BcReduce<N>::rest(r, lane);
         if (bc_writer) st.red[tc.wv][j][e_idx] = tot;
         const float dDelta = fmaf(sAq, kLn2, xf * sLB);
