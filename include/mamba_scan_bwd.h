@@ -53,7 +53,9 @@ extern "C" {
  * must be 0 (the backward of the MAMBA_SCAN_ZOH mode is not provided:
  * mamba_scan_bwd returns MAMBA_ERR_UNSUPPORTED for it). The workspace holds,
  * among others, one fp32 copy of the state per 8 time steps (about
- * batch * seqlen * dim * dstate / 2 bytes). Returns 0 for an invalid
+ * batch * seqlen * dim * dstate / 2 bytes); one such copy, batch * dim *
+ * dstate * 4 bytes, must stay below 2^31 (else mamba_scan_bwd returns
+ * MAMBA_ERR_UNSUPPORTED and this function 0). Returns 0 for an invalid
  * descriptor as well.
  */
 size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc *desc);

@@ -642,6 +642,10 @@ mamba_status scan_bwd_check(const char* who, const mamba_scan_desc* d) {
                 who);
   if (d->flags & ~0xffffu)
     return fail(MAMBA_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, d->flags & ~0xffffu);
+  // one state checkpoint (every row's N fp32 states) is addressed with 32-bit offsets
+  if (d->dim > 0 && d->batch > ((int64_t(1) << 31) - 1) / (4 * d->dstate) / d->dim)
+    return fail(MAMBA_ERR_UNSUPPORTED, "%s: batch * dim * dstate * 4 bytes must stay below 2^31",
+                who);
   return check_groups(d, who, true);
 }
 
@@ -655,9 +659,7 @@ mscan::ScanBwdPlan bwd_plan(const mamba_scan_desc* d) {
 extern "C" {
 
 size_t mamba_scan_bwd_workspace_size(const mamba_scan_desc* d) {
-  if (!d || check_desc(d, "mamba_scan_bwd_workspace_size") != MAMBA_OK || (d->flags & ~0xffffu) ||
-      check_groups(d, "mamba_scan_bwd_workspace_size", true) != MAMBA_OK)
-    return 0;
+  if (!d || scan_bwd_check("mamba_scan_bwd_workspace_size", d) != MAMBA_OK) return 0;
   return bwd_plan(d).workspace_bytes;
 }
 

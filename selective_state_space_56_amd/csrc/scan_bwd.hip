@@ -715,6 +715,37 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
   const bool bc_writer = BcReduce<N>::writer(lane);
   float* pbc = a.pBC + ((static_cast<int64_t>(tc.tile) * g.batch + tc.b) * g.seqlen + tc.t_begin) * M;
 
+  // The checkpoint of the chunk to be recomputed next (the first one's here,
+  // the others' loaded early in the previous chunk's adjoint sweep, into the
+  // registers of states it no longer needs, so that their latency is hidden).
+  float hc[N];
+  float cks = 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) hc[n] = 0.0f;
+  // (buffer loads: per chunk one resource in scalar registers, the tile's
+  // first row as the scalar offset, the lane's 16 or 4 bytes as the vector
+  // one; lanes past the last channel read zeros)
+  const int64_t row_base = tc.b * g.dim + tc.d0;
+  const uint32_t off16 = active ? static_cast<uint32_t>(tid) * 16u : kOffNone;
+  const uint32_t off4 = active ? static_cast<uint32_t>(tid) * 4u : kOffNone;
+  auto load_ck = [&](int cc) {
+    const int64_t chunk = ck0 + cc;
+    if constexpr (N % 4 == 0) {
+      const auto r = make_rsrc(a.ck + chunk * g.rows * N);
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            r, off16, static_cast<uint32_t>((q * g.rows + row_base) * 16), kNonTemporal);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hc[4 * q + k] = __uint_as_float(w[k]);
+      }
+    } else if (active) {
+      ck_load<N>(a.ck, chunk, g.rows, tc.row, hc);
+    }
+    cks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(a.ck_s + chunk * g.rows), off4, static_cast<uint32_t>(row_base * 4), 0));
+  };
+  load_ck(last);
   {
     const int nb = last & 1;
     tc.fetch(src, kIn, last * kChunk, &st.in[nb][0][0][0], regs);
@@ -740,14 +771,6 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
     // g = e^(n+1) h / dx + B from the state h before it)
     float hist[kChunk][N];
     {
-      float hc[N];
-      if (active) {
-        ck_load<N>(a.ck, ck0 + c, g.rows, tc.row, hc);
-      } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) hc[n] = 0.0f;
-      }
-      const float cks = active ? a.ck_s[(ck0 + c) * g.rows + tc.row] : 0.0f;
       if (active && cin) {
         // plus the carry-in decayed over the segment's steps before the chunk
         Decays<N, STRUCT> dk(cks, A2);
@@ -791,6 +814,7 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
 #pragma unroll
     for (int jj = 0; jj < kChunk; ++jj) {
       const int j = kChunk - 1 - jj;
+      if (c > 0 && jj == 1) load_ck(c - 1);
       if (j < valid) {
         const float xf = x_at(buf, j);
         const float u = u_at(buf, j);
@@ -868,12 +892,16 @@ __global__ __launch_bounds__(kBlock, kMainBlocksPerCU<IO>) void scan_bwd_kernel(
     }
     __syncthreads();
     // this chunk's dB / dC over the workgroup's channels
-    for (int i = tid; i < (valid < kChunk ? valid : kChunk) * M; i += kBlock) {
-      const int j = i / M, k = i % M;
-      float sum = 0.0f;
+    {
+      const auto rbc = make_rsrc(pbc + static_cast<int64_t>(c) * kChunk * M);
+      for (int i = tid; i < (valid < kChunk ? valid : kChunk) * M; i += kBlock) {
+        const int j = i / M, k = i % M;
+        float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kBlock / 64; ++w) sum += st.red[w][j][k];
-      pbc[static_cast<int64_t>(c * kChunk + j) * M + k] = sum;
+        for (int w = 0; w < kBlock / 64; ++w) sum += st.red[w][j][k];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rbc,
+                                              static_cast<uint32_t>(i) * 4u, 0, 0);
+      }
     }
     if (c > 0) {
       tc.land(kIn, &st.in[buf ^ 1][0][0][0], regs);

@@ -273,6 +273,12 @@ def test_scan_bwd_validation(lib):
     assert "mamba_scan_bwd: desc is NULL" in err(lib)
     assert bwd(lib, D_(dstate=32), ws=40, ws_bytes=need) == UNSUPPORTED
     assert bwd(lib, D_(flags=1 << 20), ws=40, ws_bytes=need) == INVALID
+    # one state checkpoint (batch * dim * dstate * 4 bytes) must stay below 2^31
+    big = D_(batch=6554, seqlen=8, dim=5120)
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(big)) == 0
+    assert bwd(lib, big, ws=40, ws_bytes=need) == UNSUPPORTED
+    assert "below 2^31" in err(lib)
+    assert lib.mamba_scan_bwd_workspace_size(ctypes.byref(D_(batch=6553, seqlen=8, dim=5120))) > 0
     for name in ["x", "delta", "A", "B", "C", "dout", "dx", "ddelta", "dA", "dB", "dC"]:
         assert bwd(lib, d, ws=40, ws_bytes=need, **{name: None}) == INVALID, name
         assert f"{name} is NULL" in err(lib)
