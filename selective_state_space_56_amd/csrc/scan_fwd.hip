@@ -147,13 +147,14 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
 // LDS staging of one chunk of kChunk steps for the workgroup's channel tile:
 // x, Delta_raw and z as stored (raw io values) and B_t, C_t widened to fp32.
 // Two buffers: the next chunk is fetched while the current one is computed.
-// With Y, the outputs y of a chunk are collected in LDS and written to HBM as
-// one tile at the start of the next chunk.
-template <int N, class IO, bool Y, int NIN>
+// The outputs y leave from registers, one store per lane and step (a wave
+// writes 64 consecutive channels of one step): on the 8 x 2048 x 5120 layer
+// this measured 314-317 against 320-324 us per call for y collected in LDS
+// and written as one tile per chunk, and it keeps 8 KB of LDS free.
+template <int N, class IO, int NIN>
 struct __align__(16) Stage {
   typename IO::raw in[2][NIN][kChunk][kBlock];  // [buffer][x, Delta_raw (, z)][step][channel]
   float bc[2][kChunk][2 * N];                 // [buffer][step][B_0..B_{N-1}, C_0..C_{N-1}]
-  typename IO::raw yo[Y ? 2 : 1][Y ? kChunk : 1][kBlock];  // [buffer][step][channel]
 };
 
 
@@ -197,12 +198,14 @@ constexpr int kFoldInOutputMax = 16;
 #define MSCAN_PIN_STEPS 1
 #endif
 
-// Occupancy targets in waves per SIMD: the output pass stages x, Delta_raw, z
-// and y (35 KB of LDS per 256 lanes), so at most four waves per SIMD fit in a
-// CU's 160 KB; the aggregate pass stages x and Delta_raw only and runs five.
-// The launch bound (in workgroups per CU: four SIMDs per CU) keeps the
-// compiler within the matching register budget (128 or 102 vector registers
-// per lane) instead of hoisting loads of later steps.
+// Occupancy targets in waves per SIMD: four for the output pass, five for the
+// aggregate pass. The launch bound (in workgroups per CU: four SIMDs per CU)
+// keeps the compiler within the matching register budget (128 or 102 vector
+// registers per lane) instead of hoisting loads of later steps. More output
+// waves (five or six, 96 or 80 registers, no spills in the structured loop)
+// measured 6-15 % slower on the 8 x 2048 x 5120 layer with the library's
+// segment plan and with 8-12 equal segments: the long-running workgroups
+// share their SIMD with more waves, and the issue rate does not rise.
 template <int MODE>
 constexpr int kWavesPerSimd = MODE == kOutput ? MSCAN_OUT_WAVES : MSCAN_AGG_WAVES;
 template <int MODE>
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   constexpr bool kC = MODE == kOutput;
   constexpr int kTileElems = kChunk * 2 * N;
   constexpr int kBcPer = (kTileElems + kBlock - 1) / kBlock;  // B/C tile elements per thread
-  __shared__ Stage<N, IO, MODE == kOutput, kZ ? 3 : 2> st;
+  __shared__ Stage<N, IO, kZ ? 3 : 2> st;
   constexpr int kZi = kZ ? 2 : 0;  // z's slot (unused without the gate)
 
   const int tid = threadIdx.x;
@@ -331,7 +334,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
   const uint32_t lo_x = CW != 0 ? tile_lane_offset<IO, kCW>(rbx, valid_bytes) : 0u;
   const uint32_t lo_d = CW != 0 ? tile_lane_offset<IO, kCW>(rbd, valid_bytes) : 0u;
   const uint32_t lo_z = CW != 0 && kZ ? tile_lane_offset<IO, kCW>(rbz, valid_bytes) : 0u;
-  const uint32_t lo_o = CW != 0 ? tile_lane_offset<IO, kCW>(rbo, valid_bytes) : 0u;
   const int wv = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index, wave-uniform
   // first element of the tile in the segment's first step, per tensor
   const raw* x0 = x + step0 * g.sx + d0;
@@ -382,11 +384,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       if (i < kTileElems) st.bc[nb][i / (2 * N)][i % (2 * N)] = bcv[r];
     }
   };
-  // y tile of the chunk at step t1 from LDS buffer yb to HBM
-  auto put_y = [&](int yb, uint32_t t1) {
-    store_tile<IO, CW>(out0 + static_cast<int64_t>(t1) * g.so, steps - t1, rbo,
-                       &st.yo[yb][0][0], lo_o, ch_off);
-  };
   auto land = [&](int nb) {
     if constexpr (CW == 0) {
       store_tile_regs<IO>(rgx, &st.in[nb][0][0][0]);
@@ -407,16 +404,17 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
     wait_vmem();
     __syncthreads();
     const uint32_t n_chunks = (steps + kChunk - 1) / kChunk;
-    // One chunk: write out the previous chunk's y tile, start fetching the
-    // next chunk, run the steps, then land the next chunk's B/C and wait for
-    // its copies. MORE: not the last chunk (so all kChunk steps are valid).
+    // One chunk: start fetching the next chunk, run the steps (each storing
+    // its y), then land the next chunk's B/C and wait for its copies. MORE:
+    // not the last chunk (so all kChunk steps are valid).
     auto chunk = [&](uint32_t c, auto more_tag, auto full_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       constexpr bool FULL = decltype(full_tag)::value;
       const int buf = c & 1;
       const uint32_t t0 = c * kChunk;
-      if (MODE == kOutput && c > 0)
-        put_y(buf ^ 1, t0 - kChunk);
+      // y of step t0 + j: channel ch_off (kOffNone past the last channel:
+      // dropped) of row j from here
+      const auto yrs = make_rsrc(out0 + static_cast<int64_t>(t0) * g.so);
       if (MORE) {
         fetch(buf ^ 1, t0 + kChunk);
         fetch_bc(t0 + kChunk);
@@ -439,7 +437,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           read_bc<N>(st.bc[buf][js], bc, kC);
           const raw y =
               update<N, IO, MODE, GATE, KSTRUCT, PATHS == kPathGeneralZoh>(fe, bc, A2, Dd, h, dx_prev);
-          if (MODE == kOutput) st.yo[buf][js][tid] = y;
+          if (MODE == kOutput) IO::bstore(y, yrs, ch_off, static_cast<uint32_t>(js) * rbo);
           if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
           // This step's state update completes here, not after later steps'
@@ -469,10 +467,6 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
       chunk(n_chunks - 1, std::false_type{}, std::true_type{});
     else
       chunk(n_chunks - 1, std::false_type{}, std::false_type{});
-    if (MODE == kOutput) {
-      const uint32_t last = n_chunks - 1;
-      put_y(last & 1, last * kChunk);
-    }
     if (KSTRUCT) {
 #pragma unroll
       for (int n = 0; n < N; ++n) h[n] *= dx_prev;  // back from g to h
