@@ -106,8 +106,13 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
                                                    float& dx_prev) {
   float y;
   if (STRUCTURED) {
+    // alpha_n = rho e^(n+1) as one chain of multiplications (N of them; the
+    // two-chain form of scaled_powers, N + 1 multiplications, measured ~1 %
+    // slower here)
     float alpha[N];
-    scaled_powers<N>(f.e, dx_prev * f.rdx, alpha);
+    alpha[0] = dx_prev * f.rdx * f.e;
+#pragma unroll
+    for (int n = 1; n < N; ++n) alpha[n] = alpha[n - 1] * f.e;
     dx_prev = f.dx;
     float acc = 0.0f;
 #pragma unroll
@@ -147,10 +152,11 @@ __device__ __forceinline__ typename IO::raw update(const FrontEnd& f, const floa
 // LDS staging of one chunk of kChunk steps for the workgroup's channel tile:
 // x, Delta_raw and z as stored (raw io values) and B_t, C_t widened to fp32.
 // Two buffers: the next chunk is fetched while the current one is computed.
-// The outputs y leave from registers, one store per lane and step (a wave
-// writes 64 consecutive channels of one step): on the 8 x 2048 x 5120 layer
-// this measured 314-317 against 320-324 us per call for y collected in LDS
-// and written as one tile per chunk, and it keeps 8 KB of LDS free.
+// The outputs y leave from registers, one non-temporal store per lane and
+// step (a wave writes 64 consecutive channels of one step): on the
+// 8 x 2048 x 5120 layer this measured 314-317 against 320-324 us per call for
+// y collected in LDS and written as one tile per chunk, and it keeps 8 KB of
+// LDS free.
 template <int N, class IO, int NIN>
 struct __align__(16) Stage {
   typename IO::raw in[2][NIN][kChunk][kBlock];  // [buffer][x, Delta_raw (, z)][step][channel]
@@ -437,7 +443,8 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           read_bc<N>(st.bc[buf][js], bc, kC);
           const raw y =
               update<N, IO, MODE, GATE, KSTRUCT, PATHS == kPathGeneralZoh>(fe, bc, A2, Dd, h, dx_prev);
-          if (MODE == kOutput) IO::bstore(y, yrs, ch_off, static_cast<uint32_t>(js) * rbo);
+          if (MODE == kOutput)
+            IO::template bstore<kNonTemporal>(y, yrs, ch_off, static_cast<uint32_t>(js) * rbo);
           if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
           // This step's state update completes here, not after later steps'
