@@ -58,11 +58,9 @@ struct F32Io {
                                               uint32_t soff) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
   }
-  // AUX: cache policy bits of the store (0, or non-temporal)
-  template <int AUX = 0>
   static __device__ __forceinline__ void bstore(raw v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                 uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
   }
   static __device__ __forceinline__ float to_f32(raw v) { return v; }
   static __device__ __forceinline__ raw from_f32(float v) { return v; }
@@ -90,10 +88,9 @@ struct Bf16Io {
                                               uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   }
-  template <int AUX = 0>
   static __device__ __forceinline__ void bstore(raw v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                 uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, AUX);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
   }
   // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
   static __device__ __forceinline__ raw from_f32(float v) {
