@@ -65,6 +65,18 @@ enum Mode { kOutput = 0, kAggregate = 1 };
 constexpr float kDxFloor = 1e-20f;
 
 
+// One output value to HBM with the non-temporal hint (y is not read again
+// here): lane offset voff (kOffNone: dropped) plus soff bytes into r.
+template <class IO>
+__device__ __forceinline__ void store_y_nt(typename IO::raw v, __amdgpu_buffer_rsrc_t r,
+                                           uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(typename IO::raw) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, kNonTemporal);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff,
+                                          kNonTemporal);
+}
+
 // Per-step values that do not depend on the state: computed one step ahead
 // of the state update so the two overlap.
 struct FrontEnd {
@@ -443,8 +455,7 @@ __global__ __launch_bounds__(kBlock, kMinBlocksPerCU<MODE>) void scan_segment_ke
           read_bc<N>(st.bc[buf][js], bc, kC);
           const raw y =
               update<N, IO, MODE, GATE, KSTRUCT, PATHS == kPathGeneralZoh>(fe, bc, A2, Dd, h, dx_prev);
-          if (MODE == kOutput)
-            IO::template bstore<kNonTemporal>(y, yrs, ch_off, static_cast<uint32_t>(js) * rbo);
+          if (MODE == kOutput) store_y_nt<IO>(y, yrs, ch_off, static_cast<uint32_t>(js) * rbo);
           if (MODE == kAggregate) dsum += fe.Delta;
           fe = fn;
           // This step's state update completes here, not after later steps'
