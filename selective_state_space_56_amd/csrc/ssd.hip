@@ -101,6 +101,9 @@ __device__ __forceinline__ bf16x8 lds_kmajor(const uint16_t* T, int ld, int lane
 struct SsdDims {
   int64_t batch, seqlen, nheads, ngroups;
   int chunks;
+  // no initial state: the state entering chunk 0 is zero, so it is neither
+  // handed over nor multiplied in
+  bool zero_entry;
 };
 
 // Delta_t = softplus(dt + bias) of the workgroup's chunk, one step per thread
@@ -225,8 +228,9 @@ __global__ __launch_bounds__(kThreads, 3) void ssd_chunk_state_kernel(
     const float ell_last = s_ell[kQ - 1];
     // the state entering this chunk (the row offset of register r is a
     // constant); non-temporal (aux 2): it is read once, by the chunk scan, and
-    // should not push the inputs read again out of the caches
-    {
+    // should not push the inputs read again out of the caches. A zero state
+    // entering chunk 0 is not written (the chunk scan skips it).
+    if (c > 0 || !g.zero_entry) {
       const auto rs = make_rsrc(Sin + (bh * g.chunks + c) * per_head, per_head * 4);
       const uint32_t voff = static_cast<uint32_t>((4 * hi * kN + n) * 4);
 #pragma unroll
@@ -394,10 +398,14 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
     if (t >= g.seqlen) xv[k] = u16x8{};
   }
   const int64_t sin_off = (((b * g.nheads + h) * g.chunks + c) * kP) * kN;
+  // whether a state enters this chunk (uniform over the workgroup)
+  const bool inherit = c > 0 || !g.zero_entry;
+  if (inherit) {
 #pragma unroll
-  for (int k = 0; k < kSPieces; ++k)
-    sv[k] = __builtin_nontemporal_load(  // read once
-        reinterpret_cast<const f32x4*>(Sin + sin_off + (tid + kScanThreads * k) * 4));
+    for (int k = 0; k < kSPieces; ++k)
+      sv[k] = __builtin_nontemporal_load(  // read once
+          reinterpret_cast<const f32x4*>(Sin + sin_off + (tid + kScanThreads * k) * 4));
+  }
   chunk_decay(dt, dt_bias ? dt_bias[h] : 0.0f, A[h], g, b, h, c, s_delta, s_ell, s_wave);
   // per step s: exp(ell_ref - ell_s) Delta_s, ell_ref at the end of the step's 32-step tile
   if (tid < kQ) s_v[tid] = hw_exp2((s_ell[tid | 31] - s_ell[tid]) * kLog2e) * s_delta[tid];
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
   }
   // S_in as a bf16 pair hi + lo (hi + lo = S_in to about 2^-17 relative)
 #pragma unroll
-  for (int k = 0; k < kSPieces; ++k) {
+  for (int k = 0; k < kSPieces && inherit; ++k) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int id = tid + kScanThreads * k;
     u32x2 vh, vl;
@@ -457,19 +465,21 @@ __global__ __launch_bounds__(kScanThreads, 2) void ssd_chunk_scan_kernel(
     __builtin_amdgcn_sched_barrier(0);
     f32x16 acc[2] = {};
     // inherited state: C_t S_in
+    if (inherit) {
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+      for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-      for (int kb = 0; kb < kN / 16; ++kb) {
-        acc[pt] = mfma(cf[kb], load8(&s_sh[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
-        acc[pt] = mfma(cf[kb], load8(&s_sl[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
+        for (int kb = 0; kb < kN / 16; ++kb) {
+          acc[pt] = mfma(cf[kb], load8(&s_sh[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
+          acc[pt] = mfma(cf[kb], load8(&s_sl[pt * 32 + lo][16 * kb + 8 * hi]), acc[pt]);
+        }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float f = hw_exp2(s_ell[32 * i + 8 * (r >> 2) + 4 * hi + (r & 3)] * kLog2e);
-      acc[0][r] *= f;
-      acc[1][r] *= f;
+      for (int r = 0; r < 16; ++r) {
+        const float f = hw_exp2(s_ell[32 * i + 8 * (r >> 2) + 4 * hi + (r & 3)] * kLog2e);
+        acc[0][r] *= f;
+        acc[1][r] *= f;
+      }
     }
     // every wave is done with S_in: its space takes the output tiles from here on
     __syncthreads();
@@ -610,6 +620,7 @@ hipError_t launch_ssd_fwd(const SsdProblem& p, void* workspace, hipStream_t stre
   g.nheads = p.nheads;
   g.ngroups = p.ngroups;
   g.chunks = static_cast<int>((p.seqlen + kQ - 1) / kQ);
+  g.zero_entry = p.h0 == nullptr;
   const auto* x = static_cast<const uint16_t*>(p.x);
   const auto* dt = static_cast<const uint16_t*>(p.dt);
   const auto* B = static_cast<const uint16_t*>(p.B);
