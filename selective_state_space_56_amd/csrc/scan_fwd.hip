@@ -774,18 +774,20 @@ ScanPlan plan_scan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int f
   seg_len = (seg_len + kChunk - 1) / kChunk * kChunk;
   segs = (seqlen + seg_len - 1) / seg_len;
   // Long last segment: with few segments and about two rounds of output
-  // workgroups, the others get about 2 / 7 of the last one's length. The
+  // workgroups, the others get about 2 / 9 of the last one's length. The
   // aggregate pass, which skips the last segment, then scans fewer steps, and
   // the output pass starts the long segment first, so it runs on while the
   // shorter ones drain. On the 8 x 2048 x 5120 layer: 11 segments of 144 steps
   // and one of 464, against 11 of 176 and one of 112, took 0.308 against
-  // 0.326 ms per call. With 102 segments (131,072 tokens) the saving is small
+  // 0.326 ms per call; 11 of 136 and one of 552 (this rule) took 307-309
+  // against 310-315 us for 144 + 464, and last lengths of 376, 640 and 728
+  // were slower. With 102 segments (131,072 tokens) the saving is small
   // and a longer last segment held the output launch back, so this stays
   // within kFoldInOutputMax segments. Forced segment counts keep equal
   // lengths (the backward's plan relies on them).
   if (forced_segments <= 0 && segs > 2 && segs <= kFoldInOutputMax &&
       2 * segs * blocks >= 3 * slots) {
-    const int64_t sl = (2 * seqlen / (2 * segs + 5) + kChunk / 2) / kChunk * kChunk;
+    const int64_t sl = (2 * seqlen / (2 * segs + 7) + kChunk / 2) / kChunk * kChunk;
     const int64_t last = seqlen - (segs - 1) * sl;
     if (sl >= kChunk && last >= sl && last <= max_len) seg_len = sl;
   }
