@@ -60,8 +60,10 @@ def _check(orc, w, inp, width, with_bias=True, with_state=True, channels=None):
 
 
 @pytest.mark.parametrize("batch,L,dim,width,io", [
-    (2, 300, 256, 4, "bf16"),     # 16-byte channel groups
-    (2, 300, 256, 4, "f32"),
+    (2, 300, 256, 4, "bf16"),     # 8-byte channel groups (4 bf16)
+    (2, 150, 20, 4, "bf16"),      # 4-channel groups, rows not whole 16-byte pieces
+    (1, 97, 132, 3, "bf16"),      # 4-channel groups, partial last workgroup
+    (2, 300, 256, 4, "f32"),      # 16-byte channel groups (4 fp32)
     (3, 65, 37, 4, "bf16"),       # odd channel count: one channel per thread
     (1, 129, 40, 3, "f32"),
     (2, 70, 48, 2, "bf16"),
